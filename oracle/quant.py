@@ -1,0 +1,57 @@
+"""Symmetric per-output-row int8 weight quantizer (W8A16) — oracle, test infrastructure only.
+
+The pages report a search-found int8 weight-only (W8A16) megakernel that is greedy-lossless
+(AutoMegaKernel paper index, Abstract; gist.science explainer, Technical Summary > Key
+Contributions) but do not state the granularity, scale format or rounding. The reading used
+here is the one the W8A16 workload states: symmetric int8 per output channel with an fp32
+scale equal to max|row| / 127. Every remaining choice is fixed as follows, because exact ties
+are common enough at these shapes that the choice changes bytes:
+
+    amax_n = max_k |w_nk|                       (bf16 -> fp32 is exact)
+    s_n    = fp32(amax_n / 127)                 IEEE fp32 division, round to nearest even
+    q_nk   = clamp(round_half_even(fp32(w_nk / s_n)), -127, 127)   fp32 *division*
+    amax_n == 0  ->  s_n = 0, q_n = 0
+
+Dequantized weight: w'_nk = q_nk * s_n; a W8A16 GEMV row is s_n * sum_k q_nk * x_k.
+"""
+import numpy as np
+
+from .numerics import bf16_bits_to_f32
+
+
+def quantize_rows_int8(w_bits: np.ndarray, block_rows: int = 4096):
+    """bf16 matrix (uint16 patterns, [rows, cols]) -> (int8 codes [rows, cols], fp32 scales [rows])."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    assert w_bits.ndim == 2
+    return _quantize(w_bits, bf16_bits_to_f32, block_rows)
+
+
+def quantize_rows_int8_f32(w: np.ndarray, block_rows: int = 4096):
+    """The same quantizer applied to fp32 rows (used to re-quantize dequantized weights)."""
+    w = np.asarray(w, dtype=np.float32)
+    assert w.ndim == 2
+    return _quantize(w, lambda a: a, block_rows)
+
+
+def _quantize(src: np.ndarray, widen, block_rows: int):
+    rows, cols = src.shape
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scales = np.empty(rows, dtype=np.float32)
+    for r0 in range(0, rows, block_rows):
+        r1 = min(rows, r0 + block_rows)
+        w = widen(src[r0:r1])
+        amax = np.max(np.abs(w), axis=1)
+        s = (amax / np.float32(127.0)).astype(np.float32)
+        zero = s == 0
+        s_safe = np.where(zero, np.float32(1.0), s).astype(np.float32)
+        q = np.rint(w / s_safe[:, None])  # float32 / float32 stays float32; rint = half-even
+        q = np.clip(q, -127, 127)
+        q[zero] = 0
+        codes[r0:r1] = q.astype(np.int8)
+        scales[r0:r1] = np.where(zero, np.float32(0.0), s)
+    return codes, scales
+
+
+def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """int8 codes and fp32 row scales -> fp32 weights q * s."""
+    return codes.astype(np.float32) * np.asarray(scales, dtype=np.float32)[:, None]
