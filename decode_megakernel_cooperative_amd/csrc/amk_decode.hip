@@ -1,0 +1,1004 @@
+// Persistent cooperative decode kernel for gfx950 (MI355X): one launch per token runs the
+// whole Llama forward pass — RMSNorm, QKV GEMV + RoPE + KV append, split-KV GQA attention,
+// O-projection + residual, RMSNorm + SwiGLU gate/up, down + residual, final RMSNorm + lm_head.
+//
+// Method: the decode-megakernel pages (AutoMegaKernel paper index, Abstract; gist.science
+// explainer, Technical Summary > Problem Statement and Methodology) fuse the forward pass of a
+// Llama-family model into one persistent cooperative kernel whose blocks synchronise through
+// monotonic counters instead of kernel boundaries, and prefetch weights while computing. This
+// file is an MI355X design of that idea, not a translation of the pages' CUDA:
+//
+//  * Grid: one 512-thread block per compute unit (256 on MI355X), launched cooperatively so
+//    all blocks are co-resident. Each GEMV stage splits its row pairs evenly over all 2048
+//    waves; every weight byte is streamed once with coalesced non-temporal dwordx4 loads.
+//  * Barrier: blocks arrive on 8 monotonic counters (block id mod 8, one 128-byte line each)
+//    and lanes 0..7 of wave 0 poll all 8. Counters are never reset: the target of the n-th
+//    barrier is n * (blocks per counter), with a wrap-safe compare. There are no agent-scope
+//    fences: every value that crosses blocks is written and read with agent-coherent (sc1)
+//    accesses, and a block waits for its own stores (s_waitcnt 0) before arriving. Waits are
+//    bounded; a timeout raises a device error flag and every block leaves the kernel.
+//  * Activations: the GEMV input vector of a stage (RMSNorm output, attention output, SwiGLU
+//    output) is staged in LDS as fp32 holding bf16-rounded values, in a swizzled layout so the
+//    four 16-byte LDS reads of a lane per weight chunk are bank-conflict free.
+//  * W8A16: int8 codes convert with one v_cvt_f32_i32 (SDWA byte select, sign extend) per
+//    weight and feed an fp32 FMA; the per-row fp32 scale multiplies the wave-reduced sum.
+//  * Row pairs: rows are packed at load time so that rows i and i + hd/2 of one head (a RoPE
+//    pair) and rows n of gate and up (a SwiGLU pair) are adjacent; one wave computes both rows
+//    of a pair, so the RoPE / SwiGLU / residual epilogues need no cross-wave exchange.
+//  * Attention: split-KV over (kv head, position range) units, one unit per block. The G query
+//    heads of a kv head share every K/V load. Each 16-lane row (hd 128) or 8-lane row (hd 64)
+//    scores one position per step with DPP row reductions and keeps an online softmax; rows
+//    and waves merge in registers and LDS; the last block to finish a kv head (per-head
+//    counter) merges the S split partials by log-sum-exp and writes bf16 attention outputs.
+//  * No MFMA: batch-1 decode is a matrix-vector product, far below the MFMA ridge point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "amk_kparams.h"
+
+#ifndef AMK_FINE_TRACE
+#define AMK_FINE_TRACE 0  // 1: extra trace stamps inside every layer (stage-internal timing)
+#endif
+#ifndef AMK_KCG
+#define AMK_KCG 2         // 1 KB chunk slots per GEMV item (per row)
+#endif
+#ifndef AMK_PREFETCH_ITEMS
+#define AMK_PREFETCH_ITEMS 2  // GEMV items issued before the barrier in front of a stage (1 or 2)
+#endif
+#ifndef AMK_EARLY_WO
+#define AMK_EARLY_WO 0    // 1: issue the O-projection prefetch at the start of attention
+#endif
+
+namespace amk {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// agent-coherent accesses (sc1) for data exchanged between blocks
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ldc(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ldc2(const float* p, float& a, float& b) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float(static_cast<uint32_t>(v));
+  b = __uint_as_float(static_cast<uint32_t>(v >> 32));
+}
+__device__ __forceinline__ void stc(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc16(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// An empty asm that hides a value from the optimizer. Stage functions start from an opaque
+// copy of the thread index so the compiler recomputes their (cheap) per-thread addresses
+// inside the layer loop instead of hoisting dozens of them out of it and spilling them.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Wave index as a wave-uniform (scalar) value, so per-wave work splits stay in SGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(opaque(threadIdx.x) >> 6); }
+
+// Raw buffer resource over [base, base + bytes) and a non-temporal 16-byte buffer load. A lane
+// whose voffset is kOOB (beyond the resource) receives zeros without a branch.
+constexpr int kOOB = static_cast<int>(0x80000000u);
+constexpr int kBufCacheNT = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ i32x4 ldbuf(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufCacheNT);
+}
+
+
+// ------------------------------------------------------------------------------------------
+// bf16 <-> fp32
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(int v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+__device__ __forceinline__ float bf_hi(int v) { return __uint_as_float(static_cast<uint32_t>(v) & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest, ties to even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+__device__ __forceinline__ float i8_to_f32(int v, int k) {
+  return static_cast<float>(static_cast<signed char>(static_cast<uint32_t>(v) >> (8 * k)));
+}
+
+// ------------------------------------------------------------------------------------------
+// cross-lane sums
+// ------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 2^k lanes of each aligned group (k = 3: 8 lanes, k = 4: 16 lanes), in every lane
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror: adds the other quad of each 8-lane half
+  if (LANES == 16) v += dpp<0x140>(v);  // row_mirror: adds the other half of each row
+  return v;
+}
+// v from lane (lane ^ OFF) for OFF in {8, 16, 32}, in VALU: a DPP rotate by 8 inside each row of
+// 16 lanes, or the gfx950 permlane swaps that exchange rows (16) and halves (32) of the wave.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v) {
+  if (OFF == 8) return dpp<0x128>(v);  // row_ror:8
+  const unsigned u = __float_as_uint(v);
+  if (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  v += xor_lane<16>(v);
+  v += xor_lane<32>(v);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<32>(v));
+  return v;
+}
+
+// ------------------------------------------------------------------------------------------
+// grid barrier
+// ------------------------------------------------------------------------------------------
+struct GridBarrier {
+  unsigned* ctr;
+  unsigned base;   // barriers completed by earlier launches
+  unsigned n;      // barriers completed in this launch
+  uint64_t limit;
+  unsigned* err;
+  uint64_t* trace; // optional per-block timestamps (entry, then arrival/exit of every barrier)
+  int ev;
+
+  __device__ __forceinline__ void stamp() {
+    if (trace != nullptr && threadIdx.x == 0) trace[ev] = wall_clock64();
+    ++ev;
+  }
+
+  // Arrival: waits for this block's stores (s_waitcnt 0 per wave, then the workgroup
+  // barrier) and adds one to the block's arrival counter. Loads issued after arrive() and
+  // before wait() overlap the wait (the next stage's weights are prefetched there).
+  __device__ __forceinline__ void arrive() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    stamp();
+    ++n;
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(ctr + (blockIdx.x & (kBarrierCtrs - 1)) * kCtrStride, 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Wait until every block has arrived n times. Returns false if the step must be abandoned
+  // (timeout here or an error raised by another block).
+  __device__ __forceinline__ bool wait(int* abort_lds) {
+    const unsigned tid = threadIdx.x;
+    if (tid < kBarrierCtrs && tid < gridDim.x) {
+      const unsigned per = (gridDim.x - tid + kBarrierCtrs - 1) / kBarrierCtrs;
+      const unsigned target = (base + n) * per;
+      const uint64_t t0 = wall_clock64();
+      unsigned it = 0;
+      bool bad = false;
+      while (static_cast<int>(ldc(ctr + tid * kCtrStride) - target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (((++it) & 31u) == 0) {
+          if (ldc(err) != 0u) { bad = true; break; }
+          if (wall_clock64() - t0 > limit) { stc(err, 1u); bad = true; break; }
+        }
+      }
+      if (bad) *abort_lds = 1;
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    stamp();
+    return *abort_lds == 0;
+  }
+
+  __device__ __forceinline__ bool sync(int* abort_lds) {
+    arrive();
+    return wait(abort_lds);
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// weight formats and the LDS layout of a GEMV input vector
+// ------------------------------------------------------------------------------------------
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> { static constexpr int WB = 2, CW = 512, LC = 8; };   // bf16
+template <> struct Fmt<1> { static constexpr int WB = 1, CW = 1024, LC = 16; };  // int8
+// A 1 KB weight chunk covers CW columns; lane L owns LC consecutive columns (16 bytes).
+// Column e is stored at chunk*CW + (k/4)*256 + L*4 + k%4, k = e's index inside the lane, so
+// the lane's k/4-th float4 sits at a 16-byte lane stride: conflict-free ds_read_b128.
+template <int FMT>
+__device__ __forceinline__ int swz(int e) {
+  constexpr int CW = Fmt<FMT>::CW, LC = Fmt<FMT>::LC;
+  const int ch = e / CW, r = e - ch * CW, ln = r / LC, k = r - ln * LC;
+  return ch * CW + (k >> 2) * 256 + ln * 4 + (k & 3);
+}
+template <int FMT>
+__device__ __forceinline__ int padded(int K) {
+  constexpr int CW = Fmt<FMT>::CW;
+  return (K + CW - 1) / CW * CW;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+constexpr int kMaxPairsPerThread = 8;  // vectors up to 2 * 8 * 512 = 8192 elements per pass
+
+// xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w), x from the coherent residual (or the bf16
+// embedding row for layer 0), zero padded to whole weight chunks.
+template <int FMT, bool FROM_EMBED>
+__device__ __forceinline__ void rmsnorm_to_lds(const KParams& p, const float* __restrict__ w, float* xs, float* red) {
+#pragma clang fp contract(off)
+  const int H = p.H;
+  const int tid = opaque(threadIdx.x);
+  float v[kMaxPairsPerThread][2];
+#pragma unroll
+  for (int k = 0; k < kMaxPairsPerThread; ++k) {
+    const int e = 2 * (tid + k * kThreads);
+    v[k][0] = v[k][1] = 0.f;
+    if (e < H) {
+      if (FROM_EMBED) {
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(p.embed + static_cast<size_t>(p.token) * H + e);
+        v[k][0] = bf_lo(static_cast<int>(b));
+        v[k][1] = bf_hi(static_cast<int>(b));
+      } else {
+        ldc2(p.x + e, v[k][0], v[k][1]);
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPairsPerThread; ++k) ss += v[k][0] * v[k][0] + v[k][1] * v[k][1];
+  ss = block_sum(ss, red);
+  const float ms = ss / static_cast<float>(H);
+  const float r = 1.0f / sqrtf(ms + p.eps);
+#pragma unroll
+  for (int k = 0; k < kMaxPairsPerThread; ++k) {
+    const int e = 2 * (tid + k * kThreads);
+    if (e < H) {
+      xs[swz<FMT>(e)] = round_bf16((v[k][0] * r) * w[e]);
+      xs[swz<FMT>(e + 1)] = round_bf16((v[k][1] * r) * w[e + 1]);
+    }
+  }
+  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  __syncthreads();
+}
+
+// xs <- coherent vector src[0..K) (already bf16-valued), zero padded.
+template <int FMT>
+__device__ __forceinline__ void vector_to_lds(const float* src, int K, float* xs) {
+  const int tid = opaque(threadIdx.x);
+  for (int e = 2 * tid; e < K; e += 2 * kThreads) {
+    float a, b;
+    ldc2(src + e, a, b);
+    xs[swz<FMT>(e)] = a;
+    xs[swz<FMT>(e + 1)] = b;
+  }
+  for (int e = K + tid; e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMV stage over row pairs
+// ------------------------------------------------------------------------------------------
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+constexpr int kCG = AMK_KCG;  // chunk slots per item: 2 rows x kCG x 16 B dwordx4 loads per lane
+constexpr int kSeg = 32; // pairs per operand window (lane j holds the operand of packed row 2*base + j)
+
+// Registers that carry a GEMV stage's operand window and first two items across the grid
+// barrier in front of the stage.
+struct GemvRegs {
+  i32x4 a0[kCG], a1[kCG], b0[kCG], b1[kCG];
+  float wA, wB;
+};
+
+// How one stage is split. A wave owns the contiguous pair range [pa, pb), processed in
+// segments of at most kSeg pairs. Inside a segment, pair k's chunks occupy slots
+// [k*cpp, k*cpp + nch) of a padded slot space (cpp = chunks per pair rounded so that items of
+// kCG slots never straddle a pair unevenly); an item is kCG consecutive slots. Slots past a
+// row's end or past the segment read zeros, so every item issues the same 8 loads.
+struct GemvPlan {
+  int RB;   // bytes per row
+  int nch;  // 1 KB chunks per row
+  int cpp;  // padded slots per pair: 1, 2 or 4 when nch <= kCG, else a multiple of kCG
+  int pa, pb;
+};
+
+template <int FMT>
+__device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave) {
+  GemvPlan g;
+  g.RB = K * Fmt<FMT>::WB;
+  g.nch = (g.RB + 1023) >> 10;
+  g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
+  const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+  g.pa = static_cast<int>((static_cast<int64_t>(npairs) * gw) / NW);
+  g.pb = static_cast<int>((static_cast<int64_t>(npairs) * (gw + 1)) / NW);
+  return g;
+}
+
+// Position in the slot space of a segment: pair k (relative to the segment base) and slot ch.
+struct Cursor {
+  int k, ch;
+  __device__ __forceinline__ void advance(int cpp) {
+    const int n = ch + 1;
+    const bool wrap = n == cpp;
+    ch = wrap ? 0 : n;
+    k += wrap ? 1 : 0;
+  }
+};
+
+template <int FMT>
+__device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const float* __restrict__ xl,
+                                          float& a0, float& a1) {
+  if (FMT == 1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(xl + d * 256);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a0 = __builtin_fmaf(i8_to_f32(w0[d], k), x[k], a0);
+        a1 = __builtin_fmaf(i8_to_f32(w1[d], k), x[k], a1);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(xl + h * 256);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int u0 = w0[2 * h + d], u1 = w1[2 * h + d];
+        a0 = __builtin_fmaf(bf_lo(u0), x[2 * d], a0);
+        a0 = __builtin_fmaf(bf_hi(u0), x[2 * d + 1], a0);
+        a1 = __builtin_fmaf(bf_lo(u1), x[2 * d], a1);
+        a1 = __builtin_fmaf(bf_hi(u1), x[2 * d + 1], a1);
+      }
+    }
+  }
+}
+
+// Per-pair operands for a window of 32 pairs: lane j holds the value for packed row
+// 2 * (window base) + j: A = W8A16 row scale, B = residual input (EPI_RESID) or RoPE cos
+// (even j) / sin (odd j) of the pair (EPI_QKV).
+template <int FMT, int EPI>
+__device__ __forceinline__ void load_window(const KParams& p, const float* __restrict__ Sc, int wbase,
+                                            int pb, bool resid_from_embed, float& A, float& B) {
+  const int lane = __lane_id();
+  const int row = 2 * wbase + lane;
+  A = 1.f;
+  B = 0.f;
+  if (row < 2 * pb) {
+    if (FMT == 1) A = Sc[row];
+    if (EPI == EPI_RESID) {
+      B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(p.token) * p.H + row]) : ldc(p.x + row);
+    } else if (EPI == EPI_QKV) {
+      const int half = p.hd >> 1;
+      const int i = (row >> 1) % half;
+      B = (row & 1) ? p.rope_sin[static_cast<size_t>(p.pos) * half + i] : p.rope_cos[static_cast<size_t>(p.pos) * half + i];
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1) {
+#pragma clang fp contract(off)
+  if (EPI == EPI_QKV) {
+    const int half = p.hd >> 1;
+    const int hb = pr / half, i = pr - hb * half;
+    if (hb < p.nq + p.nkv) {
+      const float c = b0, s = b1;
+      const float a = y0 * c - y1 * s;
+      const float b = y1 * c + y0 * s;
+      if (hb < p.nq) {
+        stc(p.q + hb * p.hd + i, a);
+        stc(p.q + hb * p.hd + i + half, b);
+      } else {
+        uint16_t* kp = p.kv + ((static_cast<size_t>(layer) * 2 * p.nkv + (hb - p.nq)) * p.max_ctx + p.pos) * p.hd;
+        stc16(kp + i, f32_to_bf16(a));
+        stc16(kp + i + half, f32_to_bf16(b));
+      }
+    } else {
+      const int g = hb - p.nq - p.nkv;
+      uint16_t* vp = p.kv + ((static_cast<size_t>(layer * 2 + 1) * p.nkv + g) * p.max_ctx + p.pos) * p.hd;
+      stc16(vp + i, f32_to_bf16(y0));
+      stc16(vp + i + half, f32_to_bf16(y1));
+    }
+  } else if (EPI == EPI_RESID) {
+    stc(p.x + 2 * pr, b0 + y0);
+    stc(p.x + 2 * pr + 1, b1 + y1);
+  } else if (EPI == EPI_SWIGLU) {
+    const float sg = y0 / (1.0f + expf(-y0));
+    stc(p.m + pr, round_bf16(sg * y1));
+  } else {
+    p.logits[2 * pr] = y0;
+    p.logits[2 * pr + 1] = y1;
+  }
+}
+
+// Issues the 8 loads of the item that starts at cursor c (advancing c by kCG slots). np = pairs
+// in the segment, base = first pair of the segment.
+__device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const GemvPlan& g, int base, int np,
+                                           Cursor& c, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int s = 0; s < kCG; ++s) {
+    const bool v = c.ch < g.nch && c.k < np;
+    const int off = c.ch * 1024 + lane * 16;
+    const int voff = (v && off < g.RB) ? off : kOOB;
+    // uniform by construction; readfirstlane keeps the compiler from moving it to VGPRs
+    const int soff = __builtin_amdgcn_readfirstlane(v ? 2 * (base + c.k) * g.RB : 0);
+    r0[s] = ldbuf(rs, voff, soff);
+    r1[s] = ldbuf(rs, voff, soff + g.RB);
+    c.advance(g.cpp);
+  }
+}
+
+// Accumulates the item at cursor c into (acc0, acc1); when a slot completes a pair, reduces it
+// over the wave and lane 0 runs the epilogue. Slots that read zeros add nothing.
+template <int FMT, int EPI>
+__device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
+                                             const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
+                                             float wA, float wB, Cursor& c, float& acc0, float& acc1) {
+  constexpr int CW = Fmt<FMT>::CW;
+#pragma unroll
+  for (int s = 0; s < kCG; ++s) {
+    // keep the scheduler from hoisting the conversions of all slots at once (register spills)
+    __builtin_amdgcn_sched_barrier(0);
+    chunk_fma<FMT>(r0[s], r1[s], xlane + min(c.ch, g.nch - 1) * CW, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c.ch == g.nch - 1 && c.k < np) {
+      float y0 = wave_sum(acc0), y1 = wave_sum(acc1);
+      acc0 = acc1 = 0.f;
+      const int j = 2 * c.k;
+      if (FMT == 1) {
+        y0 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j));
+        y1 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j + 1));
+      }
+      const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
+      const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
+      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1);
+    }
+    c.advance(g.cpp);
+  }
+}
+
+// Loads the operand window of the segment at `base` and issues the segment's first two items.
+template <int FMT, int EPI>
+__device__ __forceinline__ void gemv_segment_start(const KParams& p, __amdgpu_buffer_rsrc_t rs,
+                                                   const float* __restrict__ Sc, const GemvPlan& g, int base,
+                                                   int np, bool rfe, bool two, GemvRegs& R) {
+  load_window<FMT, EPI>(p, Sc, base, g.pb, rfe, R.wA, R.wB);
+  Cursor c{0, 0};
+  gemv_issue(rs, g, base, np, c, R.a0, R.a1);
+  if (two) gemv_issue(rs, g, base, np, c, R.b0, R.b1);
+}
+
+// Issues the stage's operand window and first two items; called between the arrival at the
+// barrier in front of the stage and the wait, so HBM keeps streaming while the grid syncs.
+template <int FMT, int EPI>
+__device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
+                                              const float* __restrict__ Sc, int K, int npairs, bool rfe,
+                                              GemvRegs& R) {
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
+  gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, AMK_PREFETCH_ITEMS > 1, R);
+}
+
+// Runs the stage. Items alternate between the two register buffers, each refilled two items
+// ahead of its use; the loop body is branch free apart from the per-pair epilogue, so loads
+// stay in flight across iterations.
+template <int FMT, int EPI>
+__device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __restrict__ W,
+                                         const float* __restrict__ Sc, int K, int npairs, const float* xs,
+                                         int layer, bool rfe, GemvRegs& R) {
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
+  const float* xlane = xs + __lane_id() * 4;
+  for (int base = g.pa; base < g.pb; base += kSeg) {
+    const int np = min(kSeg, g.pb - base);
+    if (base != g.pa) gemv_segment_start<FMT, EPI>(p, rs, Sc, g, base, np, rfe, true, R);
+    const int items = (np * g.cpp + kCG - 1) / kCG;
+    Cursor ci{0, 0}, cc{0, 0};
+    for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
+    if (AMK_PREFETCH_ITEMS > 1 || base != g.pa) {
+      for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
+    } else {
+      gemv_issue(rs, g, base, np, ci, R.b0, R.b1);  // second item was not prefetched
+    }
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int it = 0; it < items; it += 2) {
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1);
+      gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1);
+      gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// split-KV GQA attention
+// ------------------------------------------------------------------------------------------
+
+template <int GMAX>
+struct AttnRegs {
+  static constexpr int U = GMAX > 4 ? 2 : 4;  // position groups per wave per pipeline step
+  i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
+};
+
+// Split-KV plan of this step: block u < nkv * S owns kv head g = u / S and positions
+// [j*T, min((j+1)*T, pos+1)) with j = u % S.
+struct AttnUnit {
+  int g, j, t0, t1, ngroups;
+  bool active;
+};
+template <int HD>
+__device__ __forceinline__ AttnUnit attn_unit(const KParams& p) {
+  constexpr int PPW = 64 / (HD / 8);
+  AttnUnit a;
+  const int S = p.S > 0 ? p.S : 1;
+  const int u = blockIdx.x;
+  a.active = u < p.nkv * p.S;
+  a.g = u / S;
+  a.j = u - a.g * S;
+  a.t0 = a.j * p.T;
+  a.t1 = min(a.t0 + p.T, p.pos + 1);
+  a.ngroups = a.active ? (a.t1 - a.t0 + PPW - 1) / PPW : 0;
+  return a;
+}
+
+// K/V loads of one pipeline step of a wave: U groups of PPW positions, one position per row
+// of LPP lanes. With skip_pos, the current position (written by this step's QKV stage,
+// possibly still in flight) is left out: the prefetch in front of the barrier uses that.
+template <int HD, int U>
+__device__ __forceinline__ void attn_load(const KParams& p, const AttnUnit& a, __amdgpu_buffer_rsrc_t kr_rs,
+                                          __amdgpu_buffer_rsrc_t vr_rs, int gbase, bool skip_pos, i32x4 (&kr)[U],
+                                          i32x4 (&vr)[U]) {
+  constexpr int LPP = HD / 8, PPW = 64 / LPP;
+  const int lane = __lane_id();
+  const int ri = lane / LPP, lo = (lane % LPP) * 16;
+#pragma unroll
+  for (int uu = 0; uu < U; ++uu) {
+    const int gg = gbase + uu * kWaves;
+    const int t = a.t0 + gg * PPW + ri;
+    const bool v = gg < a.ngroups && t < a.t1 && !(skip_pos && t == p.pos);
+    const int voff = v ? t * (HD * 2) + lo : kOOB;
+    kr[uu] = ldbuf(kr_rs, voff, 0);
+    vr[uu] = ldbuf(vr_rs, voff, 0);
+  }
+}
+
+// buffer resource over the [max_ctx][HD] bf16 K (kv = 0) or V (kv = 1) block of (layer, kv head)
+template <int HD>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const KParams& p, int layer, int kv, int g) {
+  const uint16_t* base = p.kv + ((static_cast<size_t>(layer * 2 + kv) * p.nkv + g) * p.max_ctx) * HD;
+  return make_rsrc(base, static_cast<uint32_t>(p.max_ctx) * HD * 2);
+}
+
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, AttnRegs<GMAX>& R) {
+  constexpr int U = AttnRegs<GMAX>::U;
+  const int wave = wave_id();
+  const AttnUnit a = attn_unit<HD>(p);
+  const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, a.g), vr = kv_rsrc<HD>(p, layer, 1, a.g);
+  // all lanes load (out-of-range groups read zeros), so R is written on every path
+  attn_load<HD, U>(p, a, kr, vr, wave, true, R.ka, R.va);
+  attn_load<HD, U>(p, a, kr, vr, wave + kWaves * U, true, R.kb, R.vb);
+}
+
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, int* flag, AttnRegs<GMAX>& R) {
+  constexpr int kAttnU = AttnRegs<GMAX>::U;
+  constexpr int LPP = HD / 8;     // lanes per position (8 bf16 = 16 bytes per lane)
+  constexpr int PPW = 64 / LPP;   // positions per wave load
+  const float NEG_INF = -__builtin_inff();
+  const int S = p.S;
+  const int G = p.nq / p.nkv;
+  const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
+  const int li = lane % LPP, ri = lane / LPP, d0 = li * 8;
+  float* wp = smem;  // [kWaves][GMAX][HD + 2]
+  const AttnUnit a = attn_unit<HD>(p);
+  const int g = a.g, j = a.j;
+
+  if (a.active) {
+    const int t0 = a.t0, t1 = a.t1, ngroups = a.ngroups;
+    const __amdgpu_buffer_rsrc_t kb = kv_rsrc<HD>(p, layer, 0, g);
+    const __amdgpu_buffer_rsrc_t vb = kv_rsrc<HD>(p, layer, 1, g);
+    i32x4 (&KA)[kAttnU] = R.ka;
+    i32x4 (&VA)[kAttnU] = R.va;
+    i32x4 (&KB)[kAttnU] = R.kb;
+    i32x4 (&VB)[kAttnU] = R.vb;
+    const int step = kWaves * kAttnU;
+    // the current position was left out of the prefetch (it was being written): load it now,
+    // branch free (lanes of other positions read out of range and keep their data)
+#pragma unroll
+    for (int uu = 0; uu < kAttnU; ++uu) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int gg = wave + b * step + uu * kWaves;
+        const int t = t0 + gg * PPW + ri;
+        const bool here = gg < ngroups && t == p.pos;
+        const int voff = here ? t * (HD * 2) + li * 16 : kOOB;
+        const i32x4 k = ldbuf(kb, voff, 0), v = ldbuf(vb, voff, 0);
+        if (b == 0) {
+          KA[uu] = here ? k : KA[uu];
+          VA[uu] = here ? v : VA[uu];
+        } else {
+          KB[uu] = here ? k : KB[uu];
+          VB[uu] = here ? v : VB[uu];
+        }
+      }
+    }
+    auto load = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
+      attn_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
+    };
+
+    float qv[GMAX][8];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < G) {
+        const float* qp = p.q + (g * G + h) * HD + d0;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) ldc2(qp + i, qv[h][i], qv[h][i + 1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[h][i] = 0.f;
+      }
+    }
+    float mr[GMAX], lr[GMAX], acc[GMAX][8];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      mr[h] = NEG_INF;
+      lr[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    }
+
+    auto compute = [&](int gbase, const i32x4 (&kr)[kAttnU], const i32x4 (&vr)[kAttnU]) {
+      float s[kAttnU][GMAX];
+#pragma unroll
+      for (int uu = 0; uu < kAttnU; ++uu) {
+        const int gg = gbase + uu * kWaves;
+        const bool valid = gg < ngroups && (t0 + gg * PPW + ri) < t1;
+        float kf[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          kf[2 * d] = bf_lo(kr[uu][d]);
+          kf[2 * d + 1] = bf_hi(kr[uu][d]);
+        }
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[h][i], kf[i], dot);
+          dot = group_sum<LPP>(dot);
+          s[uu][h] = valid ? dot * p.attn_scale : NEG_INF;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) continue;
+        float mnew = mr[h];
+#pragma unroll
+        for (int uu = 0; uu < kAttnU; ++uu) mnew = fmaxf(mnew, s[uu][h]);
+        if (mnew == NEG_INF) continue;
+        const float corr = (mr[h] == NEG_INF) ? 0.f : __expf(mr[h] - mnew);
+        lr[h] *= corr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
+#pragma unroll
+        for (int uu = 0; uu < kAttnU; ++uu) {
+          const float pe = (s[uu][h] == NEG_INF) ? 0.f : __expf(s[uu][h] - mnew);
+          lr[h] += pe;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            acc[h][2 * d] = __builtin_fmaf(pe, bf_lo(vr[uu][d]), acc[h][2 * d]);
+            acc[h][2 * d + 1] = __builtin_fmaf(pe, bf_hi(vr[uu][d]), acc[h][2 * d + 1]);
+          }
+        }
+        mr[h] = mnew;
+      }
+    };
+
+    // two buffers in flight; loads past the unit read zeros, so the loop body has no branch
+    for (int gb = wave; gb < ngroups; gb += 2 * step) {
+      compute(gb, KA, VA);
+      load(gb + 2 * step, KA, VA);
+      compute(gb + step, KB, VB);
+      load(gb + 3 * step, KB, VB);
+    }
+
+    // merge the rows of the wave (each row saw different positions)
+    auto merge_rows = [&](auto off_tag) {
+      constexpr int OFF = decltype(off_tag)::value;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) continue;
+        const float mo = xor_lane<OFF>(mr[h]), lo = xor_lane<OFF>(lr[h]);
+        const float M = fmaxf(mr[h], mo);
+        const float ea = (mr[h] == NEG_INF) ? 0.f : __expf(mr[h] - M);
+        const float eb = (mo == NEG_INF) ? 0.f : __expf(mo - M);
+        lr[h] = lr[h] * ea + lo * eb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * ea + xor_lane<OFF>(acc[h][i]) * eb;
+        mr[h] = M;
+      }
+    };
+    if (LPP == 8) merge_rows(std::integral_constant<int, 8>{});
+    merge_rows(std::integral_constant<int, 16>{});
+    merge_rows(std::integral_constant<int, 32>{});
+    if (ri == 0) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) continue;
+        float* dst = wp + (wave * GMAX + h) * (HD + 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[d0 + i] = acc[h][i];
+        if (li == 0) {
+          dst[HD] = mr[h];
+          dst[HD + 1] = lr[h];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (!a.active) return;
+
+  // merge the waves of the block -> this unit's partial
+  for (int t = tid; t < G * HD; t += kThreads) {
+    const int h = t / HD, d = t - h * HD;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp[(w * GMAX + h) * (HD + 2) + HD]);
+    float A = 0.f, Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* src = wp + (w * GMAX + h) * (HD + 2);
+      const float mw = src[HD];
+      const float e = (mw == NEG_INF) ? 0.f : __expf(mw - M);
+      A += src[d] * e;
+      Lsum += src[HD + 1] * e;
+    }
+    const size_t slot = static_cast<size_t>(g * G + h) * p.s_cap + j;
+    stc(p.pacc + slot * HD + d, A);
+    if (d == 0) {
+      stc(p.pml + slot * 2, M);
+      stc(p.pml + slot * 2 + 1, Lsum);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(p.gctr + g * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (old == static_cast<unsigned>(S - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+
+  // last block of this kv head: merge the S split partials of its G heads
+  if (tid == 0) stc(p.gctr + g * kCtrStride, 0u);
+  // threads own (head, dim pair) items and, RW ways, the splits; their partial sums are loaded
+  // first so they travel together with the split maxima and sums
+  const int items = G * (HD / 2);
+  int RW = 1;
+  while (RW * 2 * items <= kThreads) RW *= 2;
+  constexpr int kBatch = 16;
+  const int it = tid % items, r = tid / items;
+  const int hh = it / (HD / 2), dd = 2 * (it - hh * (HD / 2));
+  const size_t hbase = static_cast<size_t>(g * G + hh) * p.s_cap;
+  float v0[kBatch], v1[kBatch];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    const int jj = r + b * RW;
+    v0[b] = v1[b] = 0.f;
+    if (r < RW && jj < S) ldc2(p.pacc + (hbase + jj) * HD + dd, v0[b], v1[b]);
+  }
+  // one wave per head turns the split maxima / sums into merge weights e^(m_j - M) / L
+  float* wts = smem;                 // [G][S]
+  float* part = smem + G * S;        // [RW][items][2]
+  if (wave < G) {
+    const size_t base = static_cast<size_t>(g * G + wave) * p.s_cap;
+    float M = NEG_INF;
+    for (int jj = lane; jj < S; jj += 64) M = fmaxf(M, ldc(p.pml + (base + jj) * 2));
+    M = wave_max(M);
+    float Lsum = 0.f;
+    for (int jj = lane; jj < S; jj += 64) {
+      float mj, lj;
+      ldc2(p.pml + (base + jj) * 2, mj, lj);
+      const float e = (mj == NEG_INF) ? 0.f : __expf(mj - M);
+      wts[wave * S + jj] = e;
+      Lsum += lj * e;
+    }
+    Lsum = wave_sum(Lsum);
+    const float inv = 1.0f / Lsum;
+    for (int jj = lane; jj < S; jj += 64) wts[wave * S + jj] *= inv;
+  }
+  __syncthreads();
+  if (r < RW) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int jj = r + b * RW;
+      if (jj < S) {
+        a0 += v0[b] * wts[hh * S + jj];
+        a1 += v1[b] * wts[hh * S + jj];
+      }
+    }
+    for (int jb = r + kBatch * RW; jb < S; jb += RW) {  // only when S > kBatch * RW
+      float x0, x1;
+      ldc2(p.pacc + (hbase + jb) * HD + dd, x0, x1);
+      a0 += x0 * wts[hh * S + jb];
+      a1 += x1 * wts[hh * S + jb];
+    }
+    part[(r * items + it) * 2] = a0;
+    part[(r * items + it) * 2 + 1] = a1;
+  }
+  __syncthreads();
+  for (int i2 = tid; i2 < items; i2 += kThreads) {
+    float a0 = 0.f, a1 = 0.f;
+    for (int rr = 0; rr < RW; ++rr) {
+      a0 += part[(rr * items + i2) * 2];
+      a1 += part[(rr * items + i2) * 2 + 1];
+    }
+    const int h = i2 / (HD / 2), d = 2 * (i2 - h * (HD / 2));
+    stc(p.o + (g * G + h) * HD + d, round_bf16(a0));
+    stc(p.o + (g * G + h) * HD + d + 1, round_bf16(a1));
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// the persistent decode kernel
+// ------------------------------------------------------------------------------------------
+template <int HD, int FMT, int GMAX>
+__global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ float red[kWaves];
+  __shared__ int abort_flag, unit_flag;
+  if (threadIdx.x == 0) abort_flag = 0;
+  const unsigned err0 = ldc(p.err);
+  const unsigned base = ldc(p.epoch);
+  __syncthreads();
+  if (err0 != 0u) return;
+  GridBarrier bar{p.bctr, base, 0u, p.spin_limit, p.err,
+                  p.trace ? p.trace + static_cast<size_t>(blockIdx.x) * p.trace_stride : nullptr, 0};
+  bar.stamp();
+  float* xs = smem;
+  const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
+  const int qdim = p.nq * HD;
+  GemvRegs R;
+  AttnRegs<GMAX> AR;
+
+  gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv, p.s_qkv, p.H, qkv_pairs, false, R);
+  for (int l = 0; l < p.L; ++l) {
+    // RMSNorm -> QKV GEMV -> RoPE, KV append
+    if (l == 0) rmsnorm_to_lds<FMT, true>(p, p.norm_in, xs, red);
+    else rmsnorm_to_lds<FMT, false>(p, p.norm_in + static_cast<size_t>(l) * p.H, xs, red);
+    if (AMK_FINE_TRACE) bar.stamp();
+    gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, p.H, qkv_pairs, xs, l, false, R);
+    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
+    bar.arrive();
+    attention_prefetch<HD, GMAX>(p, l, AR);
+    if (!bar.wait(&abort_flag)) return;
+
+    // split-KV attention (+ merge by the last block of each kv head); the O-projection weights
+    // stream in meanwhile (they depend on nothing)
+    if (AMK_EARLY_WO)
+      gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, l == 0, R);
+    attention_stage<HD, GMAX>(p, l, smem, &unit_flag, AR);
+    bar.arrive();
+    if (!AMK_EARLY_WO)
+      gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, l == 0, R);
+    if (!bar.wait(&abort_flag)) return;
+
+    // O-projection + residual
+    vector_to_lds<FMT>(p.o, qdim, xs);
+    if (AMK_FINE_TRACE) bar.stamp();
+    gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, xs, l, l == 0, R);
+    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
+    bar.arrive();
+    gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, p.H, p.F, false, R);
+    if (!bar.wait(&abort_flag)) return;
+
+    // RMSNorm -> gate/up GEMV -> SwiGLU
+    rmsnorm_to_lds<FMT, false>(p, p.norm_post + static_cast<size_t>(l) * p.H, xs, red);
+    if (AMK_FINE_TRACE) bar.stamp();
+    gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, p.H, p.F, xs, l, false, R);
+    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
+    bar.arrive();
+    gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, p.H / 2, false, R);
+    if (!bar.wait(&abort_flag)) return;
+
+    // down GEMV + residual
+    vector_to_lds<FMT>(p.m, p.F, xs);
+    if (AMK_FINE_TRACE) bar.stamp();
+    gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, p.H / 2, xs, l, false, R);
+    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
+    bar.arrive();
+    if (l + 1 < p.L)
+      gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, p.H, qkv_pairs,
+                                  false, R);
+    else
+      gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, p.H, p.V / 2, false, R);
+    if (!bar.wait(&abort_flag)) return;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) stc(p.epoch, base + bar.n);
+  // final RMSNorm -> lm_head
+  rmsnorm_to_lds<FMT, false>(p, p.norm_final, xs, red);
+  gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, p.H, p.V / 2, xs, p.L, false, R);
+  __syncthreads();
+  bar.stamp();
+}
+
+// barrier microbenchmark: `iters` grid barriers in one persistent launch
+__global__ void __launch_bounds__(kThreads, 1) amk_barrier_kernel(unsigned* ctr, unsigned* err, int iters) {
+  __shared__ int abort_flag;
+  if (threadIdx.x == 0) abort_flag = 0;
+  __syncthreads();
+  GridBarrier bar{ctr, 0u, 0u, 100000000ull, err, nullptr, 0};
+  for (int i = 0; i < iters; ++i)
+    if (!bar.sync(&abort_flag)) return;
+}
+
+template __global__ void amk_decode_kernel<64, 0, 4>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 4>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 4>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 4>(const KParams);
+template __global__ void amk_decode_kernel<64, 0, 8>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 8>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 8>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 8>(const KParams);
+
+}  // namespace amk
+
+// host-visible handles of the kernel instantiations (defined in this translation unit)
+extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax) {
+  using namespace amk;
+  if (gmax == 4) {
+    if (head_dim == 64) return fmt ? (const void*)&amk_decode_kernel<64, 1, 4> : (const void*)&amk_decode_kernel<64, 0, 4>;
+    if (head_dim == 128) return fmt ? (const void*)&amk_decode_kernel<128, 1, 4> : (const void*)&amk_decode_kernel<128, 0, 4>;
+  } else if (gmax == 8) {
+    if (head_dim == 64) return fmt ? (const void*)&amk_decode_kernel<64, 1, 8> : (const void*)&amk_decode_kernel<64, 0, 8>;
+    if (head_dim == 128) return fmt ? (const void*)&amk_decode_kernel<128, 1, 8> : (const void*)&amk_decode_kernel<128, 0, 8>;
+  }
+  return nullptr;
+}
+extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle() { return (const void*)&amk::amk_barrier_kernel; }

@@ -1,0 +1,579 @@
+// Host side of the decode library: validation, weight packing and W8A16 quantization, upload,
+// RoPE tables, scratch, cooperative launch and error mapping behind the C ABI in amk.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "amk.h"
+#include "amk_kparams.h"
+
+extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax);
+extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle();
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& what) {
+  g_last_error = what;
+  return code;
+}
+
+#define HIP_TRY(call)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(e_ == hipErrorOutOfMemory ? AMK_ERR_OOM : AMK_ERR_HIP,                    \
+                  std::string(#call) + ": " + hipGetErrorString(e_));                       \
+  } while (0)
+
+constexpr uint64_t kDefaultSpinLimit = 100000000ull;  // 1 s at the 100 MHz wall clock
+
+inline float bf16_to_float(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Quantizes rows [r0, r1) of a bf16 matrix: s = amax / 127 (IEEE fp32 division), q =
+// clamp(nearbyint(w / s), -127, 127) with the default round-to-nearest-even mode.
+void quantize_rows(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8_t* codes, float* scales) {
+  for (int64_t r = r0; r < r1; ++r) {
+    const uint16_t* row = w + r * cols;
+    float amax = 0.f;
+    for (int64_t c = 0; c < cols; ++c) amax = std::max(amax, std::fabs(bf16_to_float(row[c])));
+    int8_t* out = codes + r * cols;
+    if (amax == 0.f) {
+      scales[r] = 0.f;
+      std::memset(out, 0, static_cast<size_t>(cols));
+      continue;
+    }
+    volatile float denom = 127.0f;  // keep a true division (never a reciprocal multiply)
+    const float s = amax / denom;
+    scales[r] = s;
+    for (int64_t c = 0; c < cols; ++c) {
+      float q = std::nearbyint(bf16_to_float(row[c]) / s);
+      q = std::min(127.0f, std::max(-127.0f, q));
+      out[c] = static_cast<int8_t>(q);
+    }
+  }
+}
+
+template <typename F>
+void parallel_rows(int64_t rows, F&& f) {
+  const unsigned hw = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
+  const int64_t nt = std::min<int64_t>(hw, std::max<int64_t>(1, rows / 64));
+  if (nt <= 1) {
+    f(0, rows);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int64_t t = 0; t < nt; ++t) {
+    const int64_t a = rows * t / nt, b = rows * (t + 1) / nt;
+    th.emplace_back([&f, a, b] { f(a, b); });
+  }
+  for (auto& t : th) t.join();
+}
+
+}  // namespace
+
+struct amk_model {
+  amk_config cfg{};
+  int device = 0;
+  int grid = 0;
+  int lds_bytes = 0;
+  int gmax = 4;
+  int s_cap = 1;
+  const void* kernel = nullptr;
+  uint64_t spin_limit = kDefaultSpinLimit;
+  uint64_t* trace = nullptr;
+  int32_t trace_stride = 0;
+  // device memory
+  uint8_t* weights = nullptr;
+  size_t weight_bytes = 0;
+  uint8_t* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  amk::KParams kp{};  // pointers and dims filled at load; step fields filled per call
+  // packing metadata for export
+  size_t off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0, off_lm = 0;
+  size_t off_sqkv = 0, off_so = 0, off_sgu = 0, off_sd = 0, off_slm = 0;
+};
+
+namespace {
+
+int validate_config(const amk_config* c) {
+  if (!c) return fail(AMK_ERR_INVALID_ARG, "null config");
+  if (c->hidden <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn <= 0 || c->vocab <= 0 || c->max_ctx <= 0)
+    return fail(AMK_ERR_UNSUPPORTED, "non-positive dimension");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(AMK_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads != 0) return fail(AMK_ERR_UNSUPPORTED, "n_q_heads % n_kv_heads != 0");
+  if (c->n_q_heads / c->n_kv_heads > 8) return fail(AMK_ERR_UNSUPPORTED, "more than 8 query heads per kv head");
+  if (c->hidden % 16 || c->ffn % 16 || (c->n_q_heads * c->head_dim) % 16)
+    return fail(AMK_ERR_UNSUPPORTED, "hidden, ffn and n_q_heads*head_dim must be multiples of 16");
+  if (c->hidden > 8192) return fail(AMK_ERR_UNSUPPORTED, "hidden > 8192");
+  if (c->ffn > 32768 || c->n_q_heads * c->head_dim > 32768) return fail(AMK_ERR_UNSUPPORTED, "ffn or q dim > 32768");
+  if (c->vocab % 2) return fail(AMK_ERR_UNSUPPORTED, "vocab must be even");
+  if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16) return fail(AMK_ERR_UNSUPPORTED, "weight_format");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(AMK_ERR_UNSUPPORTED, "rms_eps / rope_theta");
+  return AMK_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Row order of the packed QKV matrix: pair p = (head block hb, i) occupies rows 2p, 2p+1 and
+// holds source rows hb*hd + i and hb*hd + i + hd/2 (head blocks: nq query, nkv key, nkv value).
+// Returns the source (tensor offset 0 = q, 1 = k, 2 = v) and row for packed row r.
+inline void qkv_source(const amk_config& c, int64_t r, int* which, int64_t* src_row) {
+  const int hd = c.head_dim, half = hd / 2;
+  const int64_t pr = r / 2;
+  const int64_t hb = pr / half, i = pr % half;
+  const int64_t row_in_head = (r & 1) ? i + half : i;
+  if (hb < c.n_q_heads) {
+    *which = 0;
+    *src_row = hb * hd + row_in_head;
+  } else if (hb < c.n_q_heads + c.n_kv_heads) {
+    *which = 1;
+    *src_row = (hb - c.n_q_heads) * hd + row_in_head;
+  } else {
+    *which = 2;
+    *src_row = (hb - c.n_q_heads - c.n_kv_heads) * hd + row_in_head;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* amk_status_string(int status) {
+  static thread_local std::string s;
+  const char* base = "unknown status";
+  switch (status) {
+    case AMK_OK: base = "ok"; break;
+    case AMK_ERR_INVALID_ARG: base = "invalid argument"; break;
+    case AMK_ERR_UNSUPPORTED: base = "unsupported model or format"; break;
+    case AMK_ERR_HIP: base = "HIP runtime error"; break;
+    case AMK_ERR_COOPERATIVE: base = "persistent grid cannot be co-resident"; break;
+    case AMK_ERR_BARRIER_TIMEOUT: base = "grid barrier wait timed out on the device"; break;
+    case AMK_ERR_OOM: base = "out of memory"; break;
+  }
+  s = base;
+  if (status != AMK_OK && !g_last_error.empty()) s += ": " + g_last_error;
+  return s.c_str();
+}
+
+int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes, float* scales) {
+  if (!w || !codes || !scales) return fail(AMK_ERR_INVALID_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0) return fail(AMK_ERR_INVALID_ARG, "non-positive size");
+  parallel_rows(rows, [&](int64_t a, int64_t b) { quantize_rows(w, cols, a, b, codes, scales); });
+  return AMK_OK;
+}
+
+int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_tensors, amk_model** out) {
+  if (!out) return fail(AMK_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  int st = validate_config(cfg);
+  if (st) return st;
+  const amk_config c = *cfg;
+  const int L = c.n_layers;
+  const int expected = 2 + 9 * L + (c.tied_embeddings ? 0 : 1);
+  if (!t || n_tensors != expected) return fail(AMK_ERR_INVALID_ARG, "expected " + std::to_string(expected) + " tensors");
+  for (int i = 0; i < n_tensors; ++i)
+    if (!t[i]) return fail(AMK_ERR_INVALID_ARG, "null tensor " + std::to_string(i));
+
+  const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
+  const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd;
+  const int64_t QKV = QD + 2 * KD;
+  const bool q8 = c.weight_format == AMK_W8A16;
+  const int64_t wb = q8 ? 1 : 2;
+
+  auto m = new amk_model();
+  m->cfg = c;
+  hipError_t he = hipGetDevice(&m->device);
+  if (he != hipSuccess) { delete m; return fail(AMK_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he)); }
+  hipDeviceProp_t prop;
+  he = hipGetDeviceProperties(&prop, m->device);
+  if (he != hipSuccess) { delete m; return fail(AMK_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(he)); }
+  int coop = 0;
+  hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, m->device);
+  if (!coop) { delete m; return fail(AMK_ERR_COOPERATIVE, "device does not support cooperative launch"); }
+
+  // ---------------- layout ----------------
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  const size_t l_qkv = static_cast<size_t>(QKV * H * wb), l_o = static_cast<size_t>(H * QD * wb);
+  const size_t l_gu = static_cast<size_t>(2 * F * H * wb), l_d = static_cast<size_t>(H * F * wb);
+  const size_t off_embed = take(static_cast<size_t>(V * H * 2));
+  m->off_qkv = take(l_qkv * L);
+  m->off_o = take(l_o * L);
+  m->off_gu = take(l_gu * L);
+  m->off_d = take(l_d * L);
+  const bool lm_shares_embed = !q8 && c.tied_embeddings;
+  m->off_lm = lm_shares_embed ? off_embed : take(static_cast<size_t>(V * H * wb));
+  if (q8) {
+    m->off_sqkv = take(4 * QKV * L);
+    m->off_so = take(4 * H * L);
+    m->off_sgu = take(4 * 2 * F * L);
+    m->off_sd = take(4 * H * L);
+    m->off_slm = take(4 * V);
+  }
+  const size_t off_nin = take(4 * H * L), off_npost = take(4 * H * L), off_nfin = take(4 * H);
+  const size_t off_cos = take(4 * static_cast<size_t>(c.max_ctx) * (hd / 2));
+  const size_t off_sin = take(4 * static_cast<size_t>(c.max_ctx) * (hd / 2));
+  m->weight_bytes = off;
+
+  // grid / LDS / splits
+  m->grid = prop.multiProcessorCount;
+  m->s_cap = std::max(1, m->grid / c.n_kv_heads);
+  const int G = c.n_q_heads / c.n_kv_heads;
+  m->gmax = G <= 4 ? 4 : 8;
+  const int cw = q8 ? 1024 : 512;
+  auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
+  const int64_t xs_f = std::max({pad(H), pad(QD), pad(F)});
+  const int64_t attn_f = std::max<int64_t>(static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2),
+                                           3 * static_cast<int64_t>(G) * m->s_cap + 2 * amk::kThreads);
+  m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
+  if (m->lds_bytes > 160 * 1024) { delete m; return fail(AMK_ERR_UNSUPPORTED, "LDS need exceeds 160 KB"); }
+  m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
+  if (!m->kernel) { delete m; return fail(AMK_ERR_UNSUPPORTED, "no kernel variant"); }
+  he = hipFuncSetAttribute(m->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, m->lds_bytes);
+  if (he != hipSuccess) { delete m; return fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(he)); }
+  int per_cu = 0;
+  he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, m->kernel, amk::kThreads, m->lds_bytes);
+  if (he != hipSuccess || per_cu < 1) {
+    delete m;
+    return fail(AMK_ERR_COOPERATIVE, "persistent block does not fit on a compute unit");
+  }
+
+  // ---------------- scratch ----------------
+  size_t so = 0;
+  auto stake = [&](size_t bytes) { size_t o = so; so = align_up(so + bytes, 256); return o; };
+  const size_t s_x = stake(4 * H), s_q = stake(4 * QD), s_o = stake(4 * QD), s_m = stake(4 * F);
+  const size_t s_pacc = stake(4 * static_cast<size_t>(c.n_q_heads) * m->s_cap * hd);
+  const size_t s_pml = stake(4 * static_cast<size_t>(c.n_q_heads) * m->s_cap * 2);
+  const size_t s_gctr = stake(4 * amk::kCtrStride * static_cast<size_t>(c.n_kv_heads));
+  const size_t s_bctr = stake(4 * amk::kCtrStride * amk::kBarrierCtrs);
+  const size_t s_epoch = stake(4 * amk::kCtrStride);
+  const size_t s_err = stake(4 * amk::kCtrStride);
+  m->scratch_bytes = so;
+
+  he = hipMalloc(&m->weights, m->weight_bytes);
+  if (he != hipSuccess) { delete m; return fail(AMK_ERR_OOM, std::string("hipMalloc(weights): ") + hipGetErrorString(he)); }
+  he = hipMalloc(&m->scratch, m->scratch_bytes);
+  if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_OOM, std::string("hipMalloc(scratch): ") + hipGetErrorString(he)); }
+  he = hipMemset(m->scratch, 0, m->scratch_bytes);
+  if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_HIP, std::string("hipMemset: ") + hipGetErrorString(he)); }
+
+  // ---------------- packing + upload ----------------
+  std::vector<uint8_t> stage;
+  std::vector<int8_t> codes;
+  std::vector<float> scales, fbuf;
+  int rc = AMK_OK;
+  auto upload = [&](size_t dst, const void* src, size_t bytes) -> int {
+    hipError_t e = hipMemcpy(m->weights + dst, src, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(AMK_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    return AMK_OK;
+  };
+  // Packs rows of one layer's matrix given a row map (packed row -> source pointer).
+  auto pack_matrix = [&](int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
+                         const std::vector<const uint16_t*>& src_tensors,
+                         auto&& row_source) -> int {
+    if (q8) {
+      // quantize each source tensor in canonical order, then permute rows
+      std::vector<std::vector<int8_t>> qc(src_tensors.size());
+      std::vector<std::vector<float>> qs(src_tensors.size());
+      for (size_t k = 0; k < src_tensors.size(); ++k) {
+        int64_t r_k = 0;
+        for (int64_t r = 0; r < rows; ++r) { int w; int64_t sr; row_source(r, &w, &sr); if (w == static_cast<int>(k)) ++r_k; }
+        qc[k].resize(static_cast<size_t>(r_k * cols));
+        qs[k].resize(static_cast<size_t>(r_k));
+        int e = amk_quantize_int8(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data());
+        if (e) return e;
+      }
+      codes.resize(static_cast<size_t>(rows * cols));
+      scales.resize(static_cast<size_t>(rows));
+      for (int64_t r = 0; r < rows; ++r) {
+        int w; int64_t sr; row_source(r, &w, &sr);
+        std::memcpy(codes.data() + r * cols, qc[w].data() + sr * cols, static_cast<size_t>(cols));
+        scales[static_cast<size_t>(r)] = qs[w][static_cast<size_t>(sr)];
+      }
+      int e = upload(dst_w, codes.data(), static_cast<size_t>(rows * cols));
+      if (e) return e;
+      return upload(dst_s, scales.data(), static_cast<size_t>(rows) * 4);
+    }
+    stage.resize(static_cast<size_t>(rows * cols * 2));
+    for (int64_t r = 0; r < rows; ++r) {
+      int w; int64_t sr; row_source(r, &w, &sr);
+      std::memcpy(stage.data() + r * cols * 2, src_tensors[w] + sr * cols, static_cast<size_t>(cols * 2));
+    }
+    return upload(dst_w, stage.data(), stage.size());
+  };
+
+  rc = upload(off_embed, t[0], static_cast<size_t>(V * H * 2));
+  std::vector<float> nin(static_cast<size_t>(H * L)), npost(static_cast<size_t>(H * L)), nfin(static_cast<size_t>(H));
+  for (int l = 0; l < L && rc == AMK_OK; ++l) {
+    const uint16_t* const* lt = t + 1 + 9 * l;
+    for (int64_t i = 0; i < H; ++i) {
+      nin[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[0][i]);
+      npost[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[5][i]);
+    }
+    rc = pack_matrix(QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
+                     [&](int64_t r, int* w, int64_t* sr) { qkv_source(c, r, w, sr); });
+    if (rc) break;
+    rc = pack_matrix(H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
+                     [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
+    if (rc) break;
+    rc = pack_matrix(2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
+                     [&](int64_t r, int* w, int64_t* sr) { *w = static_cast<int>(r & 1); *sr = r >> 1; });
+    if (rc) break;
+    rc = pack_matrix(H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
+                     [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
+  }
+  if (rc == AMK_OK) {
+    for (int64_t i = 0; i < H; ++i) nfin[static_cast<size_t>(i)] = bf16_to_float(t[1 + 9 * L][i]);
+    const uint16_t* lm = c.tied_embeddings ? t[0] : t[2 + 9 * L];
+    if (!lm_shares_embed)
+      rc = pack_matrix(V, H, m->off_lm, m->off_slm, {lm}, [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
+  }
+  if (rc == AMK_OK) rc = upload(off_nin, nin.data(), nin.size() * 4);
+  if (rc == AMK_OK) rc = upload(off_npost, npost.data(), npost.size() * 4);
+  if (rc == AMK_OK) rc = upload(off_nfin, nfin.data(), nfin.size() * 4);
+  if (rc == AMK_OK) {
+    // RoPE: inv_freq_i = theta^(-2i/hd) and angle = pos * inv_freq_i in double, rounded once
+    const int64_t half = hd / 2;
+    std::vector<float> cs(static_cast<size_t>(c.max_ctx * half)), sn(cs.size());
+    for (int64_t pos = 0; pos < c.max_ctx; ++pos)
+      for (int64_t i = 0; i < half; ++i) {
+        const double inv = std::pow(static_cast<double>(c.rope_theta), -2.0 * static_cast<double>(i) / static_cast<double>(hd));
+        const double a = static_cast<double>(pos) * inv;
+        cs[static_cast<size_t>(pos * half + i)] = static_cast<float>(std::cos(a));
+        sn[static_cast<size_t>(pos * half + i)] = static_cast<float>(std::sin(a));
+      }
+    rc = upload(off_cos, cs.data(), cs.size() * 4);
+    if (rc == AMK_OK) rc = upload(off_sin, sn.data(), sn.size() * 4);
+  }
+  if (rc != AMK_OK) {
+    std::string keep = g_last_error;
+    amk_free(m);
+    g_last_error = keep;
+    return rc;
+  }
+
+  // ---------------- kernel parameters ----------------
+  amk::KParams& k = m->kp;
+  k.H = static_cast<int32_t>(H); k.L = L; k.nq = c.n_q_heads; k.nkv = c.n_kv_heads; k.hd = static_cast<int32_t>(hd);
+  k.F = static_cast<int32_t>(F); k.V = static_cast<int32_t>(V); k.max_ctx = c.max_ctx;
+  k.eps = c.rms_eps;
+  k.attn_scale = 1.0f / std::sqrt(static_cast<float>(hd));
+  uint8_t* W = m->weights;
+  k.w_qkv = W + m->off_qkv; k.w_qkv_ls = static_cast<int64_t>(l_qkv);
+  k.w_o = W + m->off_o; k.w_o_ls = static_cast<int64_t>(l_o);
+  k.w_gu = W + m->off_gu; k.w_gu_ls = static_cast<int64_t>(l_gu);
+  k.w_d = W + m->off_d; k.w_d_ls = static_cast<int64_t>(l_d);
+  k.w_lm = W + m->off_lm;
+  if (q8) {
+    k.s_qkv = reinterpret_cast<const float*>(W + m->off_sqkv); k.s_qkv_ls = QKV;
+    k.s_o = reinterpret_cast<const float*>(W + m->off_so); k.s_o_ls = H;
+    k.s_gu = reinterpret_cast<const float*>(W + m->off_sgu); k.s_gu_ls = 2 * F;
+    k.s_d = reinterpret_cast<const float*>(W + m->off_sd); k.s_d_ls = H;
+    k.s_lm = reinterpret_cast<const float*>(W + m->off_slm);
+  }
+  k.embed = reinterpret_cast<const uint16_t*>(W + off_embed);
+  k.norm_in = reinterpret_cast<const float*>(W + off_nin);
+  k.norm_post = reinterpret_cast<const float*>(W + off_npost);
+  k.norm_final = reinterpret_cast<const float*>(W + off_nfin);
+  k.rope_cos = reinterpret_cast<const float*>(W + off_cos);
+  k.rope_sin = reinterpret_cast<const float*>(W + off_sin);
+  uint8_t* S = m->scratch;
+  k.x = reinterpret_cast<float*>(S + s_x);
+  k.q = reinterpret_cast<float*>(S + s_q);
+  k.o = reinterpret_cast<float*>(S + s_o);
+  k.m = reinterpret_cast<float*>(S + s_m);
+  k.pacc = reinterpret_cast<float*>(S + s_pacc);
+  k.pml = reinterpret_cast<float*>(S + s_pml);
+  k.s_cap = m->s_cap;
+  k.gctr = reinterpret_cast<unsigned*>(S + s_gctr);
+  k.bctr = reinterpret_cast<unsigned*>(S + s_bctr);
+  k.epoch = reinterpret_cast<unsigned*>(S + s_epoch);
+  k.err = reinterpret_cast<unsigned*>(S + s_err);
+  k.spin_limit = m->spin_limit;
+  *out = m;
+  return AMK_OK;
+}
+
+int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, float* logits_out, void* stream) {
+  if (!m || !kv_cache || !logits_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
+  if (token < 0 || token >= m->cfg.vocab) return fail(AMK_ERR_INVALID_ARG, "token out of range");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
+  amk::KParams k = m->kp;
+  k.token = token;
+  k.pos = pos;
+  const int ctx = pos + 1;
+  // split-KV plan: at most s_cap splits per kv head (one attention unit per block), at least
+  // 16 positions per split
+  int T = std::max(16, (ctx + m->s_cap - 1) / m->s_cap);
+  k.T = T;
+  k.S = (ctx + T - 1) / T;
+  k.kv = static_cast<uint16_t*>(kv_cache);
+  k.logits = logits_out;
+  k.spin_limit = m->spin_limit;
+  k.trace = m->trace;
+  k.trace_stride = m->trace_stride;
+  void* args[] = {&k};
+  HIP_TRY(hipLaunchCooperativeKernel(m->kernel, dim3(m->grid), dim3(amk::kThreads), args,
+                                     static_cast<unsigned>(m->lds_bytes), static_cast<hipStream_t>(stream)));
+  return AMK_OK;
+}
+
+int amk_sync(amk_model* m, void* stream) {
+  if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  unsigned err = 0;
+  HIP_TRY(hipMemcpy(&err, m->kp.err, 4, hipMemcpyDeviceToHost));
+  if (err != 0) {
+    // counters no longer match the launch history: start over from zero
+    HIP_TRY(hipMemset(m->kp.bctr, 0, 4 * amk::kCtrStride * amk::kBarrierCtrs));
+    HIP_TRY(hipMemset(m->kp.gctr, 0, 4 * amk::kCtrStride * static_cast<size_t>(m->cfg.n_kv_heads)));
+    HIP_TRY(hipMemset(m->kp.epoch, 0, 4));
+    HIP_TRY(hipMemset(m->kp.err, 0, 4));
+    HIP_TRY(hipDeviceSynchronize());
+    return fail(AMK_ERR_BARRIER_TIMEOUT, "a decode step abandoned a grid barrier wait");
+  }
+  return AMK_OK;
+}
+
+size_t amk_kv_cache_bytes(const amk_model* m) {
+  if (!m) return 0;
+  const amk_config& c = m->cfg;
+  return static_cast<size_t>(c.n_layers) * 2 * c.n_kv_heads * static_cast<size_t>(c.max_ctx) * c.head_dim * 2;
+}
+
+int amk_get_info(const amk_model* m, amk_info* info) {
+  if (!m || !info) return fail(AMK_ERR_INVALID_ARG, "null pointer");
+  info->grid_blocks = m->grid;
+  info->block_threads = amk::kThreads;
+  info->lds_bytes = m->lds_bytes;
+  info->barriers_per_step = amk::kStagesPerLayer * m->cfg.n_layers;
+  info->weight_bytes = static_cast<int64_t>(m->weight_bytes);
+  info->scratch_bytes = static_cast<int64_t>(m->scratch_bytes);
+  info->max_splits = m->s_cap;
+  info->device = m->device;
+  return AMK_OK;
+}
+
+int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, float* scales_out) {
+  if (!m || !codes_out || !scales_out) return fail(AMK_ERR_INVALID_ARG, "null pointer");
+  const amk_config& c = m->cfg;
+  if (c.weight_format != AMK_W8A16) return fail(AMK_ERR_UNSUPPORTED, "model is not W8A16");
+  const int L = c.n_layers;
+  const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
+  const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd, QKV = QD + 2 * KD;
+  const int lm_idx = c.tied_embeddings ? 0 : 2 + 9 * L;
+  int64_t rows = 0, cols = 0, mrows = 0;
+  size_t wsrc = 0, ssrc = 0;
+  int which = -1;           // which source tensor of a fused matrix we export
+  int kind = -1;            // 0 qkv, 1 o, 2 gu, 3 d, 4 lm
+  if (idx == lm_idx) {
+    kind = 4; rows = mrows = V; cols = H; wsrc = m->off_lm; ssrc = m->off_slm;
+  } else if (idx >= 1 && idx < 1 + 9 * L) {
+    const int l = (idx - 1) / 9, o = (idx - 1) % 9;
+    switch (o) {
+      case 1: case 2: case 3:
+        kind = 0; which = o - 1; rows = (o == 1) ? QD : KD; cols = H; mrows = QKV;
+        wsrc = m->off_qkv + static_cast<size_t>(l) * QKV * H; ssrc = m->off_sqkv + 4 * static_cast<size_t>(QKV) * l; break;
+      case 4: kind = 1; rows = mrows = H; cols = QD; wsrc = m->off_o + static_cast<size_t>(l) * H * QD; ssrc = m->off_so + 4 * static_cast<size_t>(H) * l; break;
+      case 6: case 7:
+        kind = 2; which = o - 6; rows = F; cols = H; mrows = 2 * F;
+        wsrc = m->off_gu + static_cast<size_t>(l) * 2 * F * H; ssrc = m->off_sgu + 4 * static_cast<size_t>(2 * F) * l; break;
+      case 8: kind = 3; rows = mrows = H; cols = F; wsrc = m->off_d + static_cast<size_t>(l) * H * F; ssrc = m->off_sd + 4 * static_cast<size_t>(H) * l; break;
+      default: break;
+    }
+  }
+  if (kind < 0) return fail(AMK_ERR_INVALID_ARG, "tensor index is not a quantized matrix");
+  std::vector<int8_t> allc(static_cast<size_t>(mrows * cols));
+  std::vector<float> alls(static_cast<size_t>(mrows));
+  HIP_TRY(hipMemcpy(allc.data(), m->weights + wsrc, allc.size(), hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(alls.data(), m->weights + ssrc, alls.size() * 4, hipMemcpyDeviceToHost));
+  for (int64_t r = 0; r < mrows; ++r) {
+    int w = 0;
+    int64_t sr = r;
+    if (kind == 0) qkv_source(c, r, &w, &sr);
+    else if (kind == 2) { w = static_cast<int>(r & 1); sr = r >> 1; }
+    if (which >= 0 && w != which) continue;
+    std::memcpy(codes_out + sr * cols, allc.data() + r * cols, static_cast<size_t>(cols));
+    scales_out[sr] = alls[static_cast<size_t>(r)];
+  }
+  (void)rows;
+  return AMK_OK;
+}
+
+int amk_bench_barrier(int32_t iters, float* us_out) {
+  if (iters <= 0 || !us_out) return fail(AMK_ERR_INVALID_ARG, "iters <= 0 or null out");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  unsigned* buf = nullptr;
+  HIP_TRY(hipMalloc(&buf, 4 * amk::kCtrStride * (amk::kBarrierCtrs + 1)));
+  int rc = AMK_OK;
+  hipEvent_t a = nullptr, b = nullptr;
+  do {
+    hipError_t e = hipMemset(buf, 0, 4 * amk::kCtrStride * (amk::kBarrierCtrs + 1));
+    if (e == hipSuccess) e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    unsigned* ctr = buf;
+    unsigned* err = buf + amk::kCtrStride * amk::kBarrierCtrs;
+    void* args[] = {&ctr, &err, &iters};
+    if (e == hipSuccess) e = hipEventRecord(a, nullptr);
+    if (e == hipSuccess)
+      e = hipLaunchCooperativeKernel(amk_barrier_kernel_handle(), dim3(prop.multiProcessorCount), dim3(amk::kThreads),
+                                     args, 0, nullptr);
+    if (e == hipSuccess) e = hipEventRecord(b, nullptr);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    unsigned herr = 0;
+    if (e == hipSuccess) e = hipMemcpy(&herr, err, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) { rc = fail(AMK_ERR_HIP, std::string("barrier bench: ") + hipGetErrorString(e)); break; }
+    if (herr) { rc = fail(AMK_ERR_BARRIER_TIMEOUT, "barrier bench timed out"); break; }
+    *us_out = ms * 1000.f / static_cast<float>(iters);
+  } while (false);
+  if (a) hipEventDestroy(a);
+  if (b) hipEventDestroy(b);
+  hipFree(buf);
+  return rc;
+}
+
+int amk_set_spin_limit(amk_model* m, uint64_t ticks) {
+  if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
+  m->spin_limit = ticks ? ticks : kDefaultSpinLimit;
+  return AMK_OK;
+}
+
+int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block) {
+  if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
+  if (trace && events_per_block < 2 + 2 * amk::kStagesPerLayer * m->cfg.n_layers)
+    return fail(AMK_ERR_INVALID_ARG, "events_per_block too small");
+  m->trace = trace;
+  m->trace_stride = trace ? events_per_block : 0;
+  return AMK_OK;
+}
+
+int amk_free(amk_model* m) {
+  if (!m) return AMK_OK;
+  int rc = AMK_OK;
+  if (m->weights && hipFree(m->weights) != hipSuccess) rc = fail(AMK_ERR_HIP, "hipFree(weights)");
+  if (m->scratch && hipFree(m->scratch) != hipSuccess) rc = fail(AMK_ERR_HIP, "hipFree(scratch)");
+  delete m;
+  return rc;
+}
+
+}  // extern "C"

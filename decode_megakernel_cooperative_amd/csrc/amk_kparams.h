@@ -1,0 +1,56 @@
+// Parameter block of the persistent decode kernel (passed by value at launch).
+#pragma once
+#include <stdint.h>
+
+namespace amk {
+
+constexpr int kThreads = 512;          // threads per persistent block (8 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line per counter
+constexpr int kBarrierCtrs = 8;        // arrival counters (block id mod 8)
+constexpr int kStagesPerLayer = 5;     // grid barriers per layer
+
+struct KParams {
+  // model
+  int32_t H, L, nq, nkv, hd, F, V, max_ctx;
+  float eps, attn_scale;
+  // this step
+  int32_t token, pos, S, T;
+  // packed weights: per layer, rows are stored in the order the kernel consumes them
+  const uint8_t* w_qkv; int64_t w_qkv_ls;   // bytes per layer
+  const float* s_qkv;   int64_t s_qkv_ls;   // fp32 scales per layer (W8A16 only)
+  const uint8_t* w_o;   int64_t w_o_ls;
+  const float* s_o;     int64_t s_o_ls;
+  const uint8_t* w_gu;  int64_t w_gu_ls;
+  const float* s_gu;    int64_t s_gu_ls;
+  const uint8_t* w_d;   int64_t w_d_ls;
+  const float* s_d;     int64_t s_d_ls;
+  const uint8_t* w_lm;
+  const float* s_lm;
+  const uint16_t* embed;                    // bf16 [V][H]
+  const float* norm_in;                     // fp32 [L][H]
+  const float* norm_post;                   // fp32 [L][H]
+  const float* norm_final;                  // fp32 [H]
+  const float* rope_cos;                    // fp32 [max_ctx][hd/2]
+  const float* rope_sin;
+  // caller buffers
+  uint16_t* kv;                             // bf16 [L][2][nkv][max_ctx][hd]
+  float* logits;                            // fp32 [V]
+  // scratch (library-owned)
+  float* x;                                 // residual stream fp32 [H]
+  float* q;                                 // rotated queries fp32 [nq*hd]
+  float* o;                                 // attention output (bf16 values) fp32 [nq*hd]
+  float* m;                                 // SwiGLU output (bf16 values) fp32 [F]
+  float* pacc;                              // split partial sums fp32 [nq][S_cap][hd]
+  float* pml;                               // split max / sum fp32 [nq][S_cap][2]
+  int32_t s_cap;
+  unsigned* gctr;                           // per kv head split counters (stride kCtrStride)
+  unsigned* bctr;                           // barrier arrival counters (stride kCtrStride)
+  unsigned* epoch;                          // barriers completed by earlier launches
+  unsigned* err;                            // device error flag
+  uint64_t spin_limit;                      // wall-clock ticks per barrier wait
+  uint64_t* trace;                          // optional [grid][trace_stride] wall-clock stamps
+  int32_t trace_stride;
+};
+
+}  // namespace amk

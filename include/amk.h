@@ -1,0 +1,166 @@
+/*
+ * amk.h — C ABI of the MI355X (gfx950) batch-1 Llama decode library.
+ *
+ * One call of amk_decode_step runs the whole forward pass of one decoded token as ONE
+ * persistent cooperative kernel launch: RMSNorm, QKV GEMV, RoPE, GQA attention over the
+ * KV cache, O-projection, SwiGLU gate/up/down GEMVs and the lm_head GEMV, with grid-wide
+ * barriers between dependent stages. This follows the problem statement of the
+ * decode-megakernel pages: batch-1 decode is bandwidth bound, its latency floor is weight
+ * bytes over HBM bandwidth, and per-operator launches plus activation round trips through
+ * HBM keep frameworks off that floor (gist.science explainer of AutoMegaKernel, Technical
+ * Summary > Problem Statement); the megakernel runs the forward pass of a HuggingFace
+ * Llama-family model in one persistent cooperative launch (AutoMegaKernel paper index,
+ * Abstract; explainer, Technical Summary > Methodology, Layer 0).
+ *
+ * Conventions for every function:
+ *   - returns int status: AMK_OK (0) or a negative AMK_ERR_* code; no C++ exception or
+ *     longjmp crosses this boundary;
+ *   - "host" pointers are CPU memory, "device" pointers are GPU memory of the current
+ *     device (for example torch.Tensor.data_ptr() of a CUDA/HIP tensor);
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *   - amk_status_string() describes the most recent error of the calling thread.
+ */
+#ifndef AMK_H_
+#define AMK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AMK_OK 0
+#define AMK_ERR_INVALID_ARG (-1)     /* null pointer, token/pos/index out of range         */
+#define AMK_ERR_UNSUPPORTED (-2)     /* model shape or format outside the supported set    */
+#define AMK_ERR_HIP (-3)             /* a HIP runtime call failed (text via status string) */
+#define AMK_ERR_COOPERATIVE (-4)     /* the persistent grid cannot be co-resident          */
+#define AMK_ERR_BARRIER_TIMEOUT (-5) /* a grid barrier wait exceeded its bound (device)    */
+#define AMK_ERR_OOM (-6)             /* host or device allocation failed                   */
+
+#define AMK_BF16 0  /* weights stored bf16, fp32 accumulation                              */
+#define AMK_W8A16 1 /* weights int8, one fp32 scale per output row; activations bf16      */
+
+/* Model description. Weights follow HuggingFace LlamaForCausalLM: pre-norm RMSNorm,
+ * rotate-half RoPE with inv_freq_i = rope_theta^(-2i/head_dim), grouped-query attention
+ * (q head h reads kv head h / (n_q_heads / n_kv_heads)), SwiGLU MLP, no biases (biased
+ * projections are not representable, matching the pages' rejection of unsupported variants,
+ * explainer, Technical Summary > Key Contributions). */
+typedef struct {
+  int32_t hidden;          /* H                                                              */
+  int32_t n_layers;        /* L                                                              */
+  int32_t n_q_heads;       /* nq                                                             */
+  int32_t n_kv_heads;      /* nkv; nq % nkv == 0 and nq / nkv <= 8                           */
+  int32_t head_dim;        /* 64 or 128                                                      */
+  int32_t ffn;             /* F (intermediate size)                                          */
+  int32_t vocab;           /* V                                                              */
+  int32_t max_ctx;         /* KV-cache capacity in positions                                 */
+  float rms_eps;           /* RMSNorm epsilon                                                */
+  float rope_theta;        /* RoPE base                                                      */
+  int32_t tied_embeddings; /* 1: lm_head is embed_tokens                                     */
+  int32_t weight_format;   /* AMK_BF16 or AMK_W8A16                                          */
+} amk_config;
+
+typedef struct amk_model amk_model; /* opaque, library-owned */
+
+/* Launch geometry and memory of a loaded model (for tests and benchmarks). */
+typedef struct {
+  int32_t grid_blocks;          /* persistent blocks (one per compute unit)                 */
+  int32_t block_threads;        /* threads per block                                         */
+  int32_t lds_bytes;            /* dynamic LDS per block                                     */
+  int32_t barriers_per_step;    /* grid barriers inside one decode step                      */
+  int64_t weight_bytes;         /* device bytes of packed weights + scales + norms           */
+  int64_t scratch_bytes;        /* device bytes of library scratch                           */
+  int32_t max_splits;           /* upper bound on KV splits per kv head                      */
+  int32_t device;               /* HIP device the model lives on                             */
+} amk_info;
+
+/* Copies, packs, (for AMK_W8A16) quantizes and uploads a model to the current device.
+ * host_bf16_tensors: n_tensors host pointers to bf16 bit patterns (uint16), row-major
+ *   [out][in] for matrices, in canonical HF order:
+ *     embed_tokens [V][H];
+ *     per layer: input_layernorm [H], q_proj [nq*hd][H], k_proj [nkv*hd][H],
+ *       v_proj [nkv*hd][H], o_proj [H][nq*hd], post_attention_layernorm [H],
+ *       gate_proj [F][H], up_proj [F][H], down_proj [H][F];
+ *     norm [H]; lm_head [V][H] only when tied_embeddings == 0.
+ *   n_tensors must equal 2 + 9 L + (tied ? 0 : 1).
+ * W8A16 quantizes every projection and the lm_head (for tied models: a quantized copy of
+ * embed_tokens; the embedding gather keeps reading bf16) with amk_quantize_int8.
+ * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
+ * *out receives a model handle owned by the library until amk_free.
+ * Errors: INVALID_ARG (null pointers, wrong n_tensors), UNSUPPORTED (shape checks: head_dim
+ * in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd multiples of 16, vocab
+ * and hidden even, max_ctx >= 1), HIP, OOM, COOPERATIVE (no co-resident persistent grid). */
+int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_tensors,
+                     int32_t n_tensors, amk_model** out);
+
+/* Decodes one token: feeds `token` at position `pos`, writes K/V of position `pos` in every
+ * layer of `kv_cache`, attends over positions [0, pos] inclusive, and writes fp32 logits.
+ * One cooperative kernel launch, ordered on `stream`; returns once it is enqueued, the
+ * outputs are valid when the stream reaches that point.
+ * kv_cache: device bf16 [L][2 (K, V)][nkv][max_ctx][head_dim], amk_kv_cache_bytes() long,
+ *   caller-owned; slots [0, pos) must already hold this sequence's keys/values.
+ * logits_out: device fp32 [V], caller-owned.
+ * Errors (checked on the host before any HIP call): INVALID_ARG for null handle/pointers,
+ * token outside [0, V) or pos outside [0, max_ctx); HIP if the launch fails. A barrier
+ * timeout of an earlier step is reported as BARRIER_TIMEOUT by amk_sync.
+ * Concurrency: one handle must not run two steps at once (they share the scratch). */
+int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
+                    float* logits_out, void* stream);
+
+/* Waits for `stream` and reports a device-side error raised by earlier steps of this model
+ * (AMK_ERR_BARRIER_TIMEOUT), then clears it so the model is usable again. */
+int amk_sync(amk_model* m, void* stream);
+
+/* Bytes of the caller-owned KV cache: L * 2 * nkv * max_ctx * head_dim * 2. 0 for NULL. */
+size_t amk_kv_cache_bytes(const amk_model* m);
+
+/* Launch geometry and sizes of a loaded model. */
+int amk_get_info(const amk_model* m, amk_info* info);
+
+/* Copies the int8 codes and fp32 row scales the library uses for canonical tensor
+ * `tensor_index` (a W8A16 projection, or the lm_head index 2+9L / embed index 0 for a tied
+ * model) back to host memory in canonical [rows][cols] order. codes_out: host int8
+ * [rows*cols]; scales_out: host fp32 [rows]. Errors: INVALID_ARG for a tensor that is not
+ * quantized; UNSUPPORTED for an AMK_BF16 model. */
+int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes_out,
+                         float* scales_out);
+
+/* Host quantizer used by amk_load_weights (no GPU needed): symmetric int8 per output row.
+ * For row n: amax = max |w|, s = fp32(amax / 127) by IEEE division, q = clamp(round half to
+ * even(fp32(w / s)), -127, 127); an all-zero row gives s = 0 and q = 0. The pages name
+ * int8 weight-only (W8A16) megakernels without the scale rule (AutoMegaKernel paper index,
+ * Abstract; explainer, Technical Summary > Key Contributions); this per-row rule is the one
+ * the W8A16 workload states. w: host bf16 bit patterns [rows][cols]; codes: host int8
+ * [rows][cols]; scales: host fp32 [rows]. Errors: INVALID_ARG for null pointers or
+ * non-positive sizes. */
+int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
+                      float* scales);
+
+/* Measures the library's grid barrier: runs `iters` barriers in one persistent launch on
+ * the current device and stores the mean microseconds per barrier in *us_out. Synchronous. */
+int amk_bench_barrier(int32_t iters, float* us_out);
+
+/* Debug control: bound (in 100 MHz wall-clock ticks) on any single grid-barrier wait;
+ * 0 restores the default (one second). A tiny bound makes steps fail cleanly with
+ * BARRIER_TIMEOUT, which is how the timeout path is exercised. */
+int amk_set_spin_limit(amk_model* m, uint64_t ticks);
+
+/* Debug control: per-block stage timestamps. When trace is non-NULL, every later step of this
+ * model writes, for each block b, the 100 MHz wall clock into trace[b * events_per_block + e]:
+ * e = 0 at kernel entry, then the arrival and the exit of every grid barrier in order, then the
+ * end of the lm_head stage. trace: device uint64 [grid_blocks][events_per_block], caller-owned;
+ * events_per_block must be at least 2 + 2 * barriers_per_step. NULL switches tracing off.
+ * Errors: INVALID_ARG for a null handle or a too small events_per_block. */
+int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block);
+
+/* Releases every device and host resource of the handle. NULL is accepted. */
+int amk_free(amk_model* m);
+
+/* Text for a status code, including the failing HIP call of the last AMK_ERR_HIP. */
+const char* amk_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AMK_H_ */

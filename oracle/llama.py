@@ -146,7 +146,7 @@ class OracleModel:
     """
 
     def __init__(self, shape, tensors: List[np.ndarray], weight_format: int,
-                 widen_once: Optional[bool] = None):
+                 widen_once: Optional[bool] = None, threads: int = 1):
         self.shape = shape
         self.fmt = weight_format
         L = shape.n_layers
@@ -155,23 +155,24 @@ class OracleModel:
         if widen_once is None:
             widen_once = n_params <= 2_000_000_000
         self.embed_bits = np.asarray(tensors[0], dtype=np.uint16)
+        lm_bits = self.embed_bits if shape.tied else tensors[2 + 9 * L]
+        # the projections are independent; `threads` only spreads their construction
+        # (quantization / widening) over a thread pool, the arithmetic is the same
+        mats = [tensors[1 + 9 * l + o] for l in range(L) for o in (1, 2, 3, 4, 6, 7, 8)] + [lm_bits]
+        if threads > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(threads) as ex:
+                lins = list(ex.map(lambda b: Linear(b, weight_format, widen_once), mats))
+        else:
+            lins = [Linear(b, weight_format, widen_once) for b in mats]
         self.layers: List[Dict[str, object]] = []
         for l in range(L):
             t = tensors[1 + 9 * l: 1 + 9 * (l + 1)]
-            self.layers.append({
-                "w_in": bf16_bits_to_f32(t[0]),
-                "q": Linear(t[1], weight_format, widen_once),
-                "k": Linear(t[2], weight_format, widen_once),
-                "v": Linear(t[3], weight_format, widen_once),
-                "o": Linear(t[4], weight_format, widen_once),
-                "w_post": bf16_bits_to_f32(t[5]),
-                "gate": Linear(t[6], weight_format, widen_once),
-                "up": Linear(t[7], weight_format, widen_once),
-                "down": Linear(t[8], weight_format, widen_once),
-            })
+            q, k, v, o, gate, up, down = lins[7 * l: 7 * (l + 1)]
+            self.layers.append({"w_in": bf16_bits_to_f32(t[0]), "q": q, "k": k, "v": v, "o": o,
+                                "w_post": bf16_bits_to_f32(t[5]), "gate": gate, "up": up, "down": down})
         self.w_norm = bf16_bits_to_f32(tensors[1 + 9 * L])
-        lm_bits = self.embed_bits if shape.tied else tensors[2 + 9 * L]
-        self.lm_head = Linear(lm_bits, weight_format, widen_once)
+        self.lm_head = lins[-1]
         self.scale = F32(1.0) / np.sqrt(F32(shape.head_dim), dtype=F32)
 
     # --------------------------------------------------------------------------------------

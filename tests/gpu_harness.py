@@ -1,0 +1,97 @@
+"""Teacher-forced parity harness: runs the HIP decode library (through its C ABI binding) and the
+CPU oracle on the same seeded inputs and compares them step by step.
+
+Gates (per step): max |logit_gpu - logit_oracle| <= LOGIT_TOL; where the oracle's top-1 minus
+top-2 logit margin exceeds MARGIN, the greedy tokens are identical. Teacher forcing: both sides
+are always fed the oracle's token, so one legitimate near-tie flip cannot cascade.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import decode_megakernel_cooperative_amd as D
+import workloads as W
+from oracle.llama import OracleModel
+
+LOGIT_TOL = 2e-2
+MARGIN = 5e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class ParityResult:
+    max_abs: List[float] = field(default_factory=list)
+    greedy_checked: int = 0
+    greedy_mismatch: int = 0
+    tokens: List[int] = field(default_factory=list)
+
+
+def top2_margin(lg: np.ndarray) -> float:
+    a = np.partition(lg, -2)[-2:]
+    return float(abs(a[1] - a[0]))
+
+
+def build(shape, fmt: int, max_ctx: int, prefill_len: int, seed0: int = 0, oracle_threads: int = 8):
+    """Generates weights and the prefilled KV cache once, loads both sides. Returns (decoder,
+    oracle, kv_oracle numpy view)."""
+    t0 = time.time()
+    ws = W.gen_weights(shape, seed0)
+    bits = [W.bf16_bits(t) for t in ws]
+    kv = W.gen_kv_cache(shape, max_ctx, prefill_len, seed0)
+    log(f"  [{shape.name}] inputs generated in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    dec = D.Decoder(shape, ws, fmt, max_ctx, kv_cache=kv.cuda())
+    log(f"  [{shape.name}] GPU model loaded in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    orc = OracleModel(shape, bits, fmt, threads=oracle_threads)
+    log(f"  [{shape.name}] oracle built in {time.time() - t0:.1f}s")
+    del ws
+    kv_np = W.bf16_bits(kv)  # oracle mutates this host copy
+    return dec, orc, kv_np
+
+
+def run_teacher_forced(dec, orc, kv_np, shape, first_pos: int, prompt: List[int], n_greedy: int,
+                       greedy_window: Optional[int] = None, first_token: Optional[int] = None,
+                       check_kv: bool = False) -> ParityResult:
+    """prompt tokens fed at first_pos..; then n_greedy steps feeding the oracle's argmax."""
+    res = ParityResult()
+    tok = prompt[0] if prompt else first_token
+    n = len(prompt) + n_greedy
+    for i in range(n):
+        pos = first_pos + i
+        g = dec.step(tok, pos)
+        torch.cuda.synchronize()
+        dec.sync()
+        g = g.cpu().numpy()
+        o = orc.decode_step(tok, pos, kv_np)
+        d = float(np.max(np.abs(g - o)))
+        res.max_abs.append(d)
+        assert np.all(np.isfinite(g)), f"non-finite logits at pos {pos}"
+        in_window = i >= len(prompt) and (greedy_window is None or i - len(prompt) < greedy_window)
+        if in_window and top2_margin(o) > MARGIN:
+            res.greedy_checked += 1
+            res.greedy_mismatch += int(np.argmax(g) != np.argmax(o))
+        if check_kv:
+            kvg = dec.kv[:, :, :, pos].float().cpu().numpy()
+            kvo = kv_np[:, :, :, pos].astype(np.uint32) << 16
+            kvo = kvo.view(np.float32)
+            assert np.max(np.abs(kvg - kvo)) <= 0.05 * max(1.0, float(np.max(np.abs(kvo)))), f"KV mismatch at pos {pos}"
+        if i + 1 < len(prompt):
+            tok = prompt[i + 1]
+        else:
+            tok = int(np.argmax(o))
+        res.tokens.append(tok)
+        if i % 16 == 0 or i == n - 1:
+            log(f"    step {i} pos {pos}: max|dlogit| {d:.2e}")
+    return res

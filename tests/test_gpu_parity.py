@@ -1,0 +1,127 @@
+"""GPU parity of the HIP decode library against the CPU oracle (through the C ABI).
+
+Bars: quantized weights bit-exact; logits within 2e-2 max-abs at every step; identical greedy
+tokens wherever the oracle's top-2 margin exceeds 5e-2 (teacher forced). Inputs are the seeded
+synthetic workloads (random N(0, 0.02) weights in the named architectures' shapes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_megakernel_cooperative_amd as D
+import workloads as W
+from oracle.quant import quantize_rows_int8
+from gpu_harness import LOGIT_TOL, build, log, run_teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_gates(res, name):
+    worst = max(res.max_abs)
+    log(f"  {name}: worst max|dlogit| {worst:.3e}; greedy checked {res.greedy_checked}, mismatches {res.greedy_mismatch}")
+    assert worst <= LOGIT_TOL, f"{name}: logits differ by {worst}"
+    assert res.greedy_mismatch == 0, f"{name}: {res.greedy_mismatch} greedy mismatches"
+
+
+def test_smollm2_bf16_full_run():
+    """SmolLM2-135M shape, bf16 weights: 8 prompt tokens one per step, then 16 greedy steps."""
+    wl = W.WORKLOADS["smollm2-135m-bf16"]
+    dec, orc, kv = build(wl.shape, wl.weight_format, wl.max_ctx, wl.prefill_len)
+    prompt = W.gen_tokens(wl.shape, wl.prompt_len)
+    res = run_teacher_forced(dec, orc, kv, wl.shape, 0, prompt, wl.greedy_steps, check_kv=True)
+    _assert_gates(res, wl.key)
+    dec.close()
+
+
+def test_smollm2_w8a16_full_run_and_quantized_bytes():
+    """SmolLM2-135M shape, W8A16: codes/scales bit-exact; 64 prompt + 128 greedy steps (first 32
+    greedy steps under the greedy rule)."""
+    wl = W.WORKLOADS["smollm2-135m-w8a16"]
+    dec, orc, kv = build(wl.shape, wl.weight_format, wl.max_ctx, wl.prefill_len)
+    # bit-exact quantized weights for every projection and the (tied) lm_head
+    ws = W.gen_weights(wl.shape)
+    specs = W.tensor_specs(wl.shape)
+    checked = 0
+    for i, (name, dims, kind) in enumerate(specs):
+        if kind != "matrix":
+            continue
+        codes, scales = D.amk_export_quantized(dec.model, i, dims[0], dims[1])
+        c_ref, s_ref = quantize_rows_int8(W.bf16_bits(ws[i]))
+        assert np.array_equal(codes, c_ref), name
+        assert np.array_equal(scales.view(np.uint32), s_ref.view(np.uint32)), name
+        checked += 1
+    assert checked == 1 + 7 * wl.shape.n_layers
+    prompt = W.gen_tokens(wl.shape, wl.prompt_len)
+    res = run_teacher_forced(dec, orc, kv, wl.shape, 0, prompt, wl.greedy_steps, greedy_window=32)
+    _assert_gates(res, wl.key)
+    dec.close()
+
+
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+def test_hd128_gqa4_prefilled_multi_split(fmt):
+    """A small head_dim-128, 4-queries-per-kv-head model with a 300-position prefilled cache, so
+    attention runs several KV splits with a ragged last split, and ragged GEMV rows (ffn 1376
+    int8 bytes = 1.34 chunks)."""
+    shape = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0)
+    dec, orc, kv = build(shape, fmt, 340, 300, seed0=3)
+    tok = W.gen_tokens(shape, 1, seed0=3)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 300, [], 24, first_token=tok, check_kv=True)
+    _assert_gates(res, f"hd128-gqa4 fmt{fmt}")
+    dec.close()
+
+
+def test_g3_hd64_long_prefill_w8a16():
+    """G = 3 (SmolLM2-like grouping), head_dim 64, prefill 1500: many splits per kv head."""
+    shape = W.ModelShape("g3-hd64", 384, 2, 6, 2, 64, 1024, 2048, True, 10000.0)
+    dec, orc, kv = build(shape, D.AMK_W8A16, 1520, 1500, seed0=5)
+    tok = W.gen_tokens(shape, 1, seed0=5)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 1500, [], 16, first_token=tok)
+    _assert_gates(res, "g3-hd64")
+    dec.close()
+
+
+def test_determinism_and_idempotence():
+    """No float atomics: repeated identical steps give bitwise-identical logits and KV entries."""
+    wl = W.WORKLOADS["smollm2-135m-w8a16"]
+    shape = wl.shape
+    dec = D.Decoder(shape, W.gen_weights(shape), wl.weight_format, 16)
+    toks = W.gen_tokens(shape, 6)
+    for p, t in enumerate(toks[:5]):
+        dec.step(t, p)
+    outs, kvs = [], []
+    for _ in range(3):
+        lg = dec.step(toks[5], 5).clone()
+        torch.cuda.synchronize()
+        outs.append(lg.cpu())
+        kvs.append(dec.kv[:, :, :, 5].clone().cpu())
+    dec.sync()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert all(torch.equal(kvs[0], k) for k in kvs[1:])
+    dec.close()
+
+
+def test_invalid_arguments_rejected():
+    shape = W.small_shape(hidden=128, n_layers=1, n_q_heads=2, n_kv_heads=1, head_dim=64, ffn=256, vocab=256)
+    dec = D.Decoder(shape, W.gen_weights(shape), D.AMK_W8A16, 8)
+    with pytest.raises(D.AmkError) as e:
+        dec.step(256, 0)
+    assert e.value.status == D.amk.AMK_ERR_INVALID_ARG
+    with pytest.raises(D.AmkError):
+        dec.step(-1, 0)
+    with pytest.raises(D.AmkError):
+        dec.step(0, 8)
+    with pytest.raises(D.AmkError):
+        D.amk_decode_step(dec.model, 0, 0, None, dec.logits)
+    dec.step(0, 0)  # still usable
+    torch.cuda.synchronize()
+    dec.sync()
+    info = dec.info()
+    assert info.grid_blocks >= 1 and info.barriers_per_step == 5
+    assert D.amk_kv_cache_bytes(dec.model) == dec.kv.numel() * 2
+    dec.close()
+
+
+def test_barrier_microbenchmark():
+    us = D.amk_bench_barrier(2000)
+    log(f"  grid barrier: {us:.3f} us")
+    assert 0.05 < us < 20.0
