@@ -80,13 +80,16 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (F32(1.0) + np.exp(-z, dtype=F32))
 
 
-def attention_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: np.float32) -> np.ndarray:
-    """One query head over keys/values [T, hd]: softmax((K q) * scale) V, two-pass, float32."""
-    s = (np.asarray(K, dtype=F32) @ np.asarray(q, dtype=F32)) * F32(scale)
+def attention_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: np.float32, accum=F32) -> np.ndarray:
+    """One query head over keys/values [T, hd]: softmax((K q) * scale) V, two-pass.
+
+    accum = float32 (the oracle) or float64 (the same definition with float64 sums, used only
+    to measure how sensitive a workload is to summation order); the result is float32."""
+    s = (np.asarray(K, dtype=accum) @ np.asarray(q, dtype=accum)) * accum(scale)
     m = np.max(s)
-    e = np.exp(s - m, dtype=F32)
-    a = e / np.sum(e, dtype=F32)
-    return a @ np.asarray(V, dtype=F32)
+    e = np.exp(s - m, dtype=accum)
+    a = e / np.sum(e, dtype=accum)
+    return (a @ np.asarray(V, dtype=accum)).astype(F32)
 
 
 def gemv(W: "Linear", x: np.ndarray) -> np.ndarray:
@@ -123,16 +126,18 @@ class Linear:
             return self.codes[r0:r1].astype(F32)
         return bf16_bits_to_f32(self.bits[r0:r1])
 
-    def apply(self, x: np.ndarray) -> np.ndarray:
-        """x: [cols] or [n, cols] float32 -> [rows] or [n, rows] float32."""
+    def apply(self, x: np.ndarray, accum=F32) -> np.ndarray:
+        """x: [cols] or [n, cols] float32 -> [rows] or [n, rows] float32. accum = float32 (the
+        oracle) or float64 (sums in float64, rounded to float32 at the end)."""
         x = np.asarray(x, dtype=F32)
         y = np.empty(x.shape[:-1] + (self.rows,), dtype=F32)
+        xa = x.astype(accum)
         for r0 in range(0, self.rows, self.BLOCK):
             r1 = min(self.rows, r0 + self.BLOCK)
-            W = self._block(r0, r1)
-            acc = x @ W.T  # float32 sums
+            W = self._block(r0, r1).astype(accum, copy=False)
+            acc = xa @ W.T
             if self.fmt == FMT_W8A16:
-                acc = acc * self.scales[r0:r1]
+                acc = acc * self.scales[r0:r1].astype(accum)
             y[..., r0:r1] = acc
         return y
 
@@ -149,6 +154,7 @@ class OracleModel:
                  widen_once: Optional[bool] = None, threads: int = 1):
         self.shape = shape
         self.fmt = weight_format
+        self.accum = F32  # float64 only to measure a workload's sensitivity to summation order
         L = shape.n_layers
         assert len(tensors) == 2 + 9 * L + (0 if shape.tied else 1)
         n_params = sum(int(np.asarray(t).size) for t in tensors)
@@ -192,9 +198,10 @@ class OracleModel:
         for l in (range(s.n_layers) if layers is None else layers):
             W = self.layers[l]
             h = round_bf16(rmsnorm(x, W["w_in"], s.rms_eps))
-            q = W["q"].apply(h).reshape(nq, hd)
-            k = W["k"].apply(h).reshape(nkv, hd)
-            v = W["v"].apply(h).reshape(nkv, hd)
+            A = self.accum
+            q = W["q"].apply(h, A).reshape(nq, hd)
+            k = W["k"].apply(h, A).reshape(nkv, hd)
+            v = W["v"].apply(h, A).reshape(nkv, hd)
             q = apply_rope(q, cos, sin)
             k = apply_rope(k, cos, sin)
             kv[l, 0, :, pos, :] = f32_to_bf16_bits(k)
@@ -204,11 +211,11 @@ class OracleModel:
                 g = hq // G
                 Kc = bf16_bits_to_f32(kv[l, 0, g, :pos + 1, :])
                 Vc = bf16_bits_to_f32(kv[l, 1, g, :pos + 1, :])
-                o[hq] = attention_head(q[hq], Kc, Vc, self.scale)
-            x = x + W["o"].apply(round_bf16(o.reshape(-1)))
+                o[hq] = attention_head(q[hq], Kc, Vc, self.scale, A)
+            x = x + W["o"].apply(round_bf16(o.reshape(-1)), A)
             h2 = round_bf16(rmsnorm(x, W["w_post"], s.rms_eps))
-            m = round_bf16(silu(W["gate"].apply(h2)) * W["up"].apply(h2))
-            x = x + W["down"].apply(m)
+            m = round_bf16(silu(W["gate"].apply(h2, A)) * W["up"].apply(h2, A))
+            x = x + W["down"].apply(m, A)
             if trace is not None:
                 trace.setdefault("h", []).append(h)
                 trace.setdefault("q", []).append(q.reshape(-1))
@@ -219,9 +226,20 @@ class OracleModel:
         hf = round_bf16(rmsnorm(x, self.w_norm, s.rms_eps))
         if trace is not None:
             trace["hf"] = hf
-        return self.lm_head.apply(hf)
+        return self.lm_head.apply(hf, self.accum)
 
     # --------------------------------------------------------------------------------------
+    def sensitivity(self, token: int, pos: int, kv: np.ndarray, reference: Optional[np.ndarray] = None) -> float:
+        """max |logits(float32 sums) - logits(float64 sums)| for this step: how far two valid
+        summation orders of the same definition land apart. Leaves `kv` unchanged."""
+        ref = reference if reference is not None else self.decode_step(token, pos, kv.copy())
+        self.accum = np.float64
+        try:
+            alt = self.decode_step(token, pos, kv.copy())
+        finally:
+            self.accum = F32
+        return float(np.max(np.abs(ref - alt)))
+
     def prefill_logits(self, tokens: Sequence[int]) -> np.ndarray:
         """Independent full-sequence causal forward over `tokens` at positions 0..P-1 with a
         fresh cache, in matrix form: returns fp32 logits [P, vocab] (one row per position).

@@ -390,6 +390,17 @@ def test_logits_scale_statistics():
     assert abs(float(np.std(lg)) / (0.02 * math.sqrt(shape.hidden)) - 1) < 0.1
 
 
+def test_sensitivity_probe_is_small_on_shallow_models():
+    """float32 and float64 summation of the same definition agree closely on a shallow model
+    (the probe measures conditioning, it is not a second definition)."""
+    shape = W.small_shape(hidden=128, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=256, vocab=512)
+    m = L.OracleModel(shape, random_model_tensors(shape, seed=51), L.FMT_W8A16)
+    kv = fresh_kv(shape, 4)
+    before = kv.copy()
+    assert m.sensitivity(3, 0, kv) < 1e-4
+    assert np.array_equal(kv, before) and m.accum == np.float32
+
+
 def test_step_idempotent():
     shape = W.small_shape(hidden=64, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=96, vocab=100)
     m = L.OracleModel(shape, random_model_tensors(shape, seed=41, std=0.1), L.FMT_W8A16)
@@ -449,8 +460,8 @@ def _rmsnorm_eps_outside(x, w, eps):
     return (x / (np.sqrt(np.mean(x * x, dtype=F32)) + F32(eps))) * np.asarray(w, dtype=F32)
 
 
-def _attention_no_scale(q, K, V, scale):
-    return _ORIG_ATT(q, K, V, F32(1.0))
+def _attention_no_scale(q, K, V, scale, accum=F32):
+    return _ORIG_ATT(q, K, V, F32(1.0), accum)
 
 
 _ORIG_ATT = L.attention_head
