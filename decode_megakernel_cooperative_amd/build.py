@@ -42,16 +42,19 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     common = ["-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
-    kobj = os.path.join(BUILD_DIR, "amk_decode.o")
+    kobjs = []
+    for src in ("amk_decode.hip", "amk_stream.hip"):
+        kobj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        _run([cc, f"--offload-arch={ARCH}", "-O3", *common,
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", os.path.join(CSRC, src), "-o", kobj], verbose)
+        kobjs.append(kobj)
     hobj = os.path.join(BUILD_DIR, "amk_host.o")
-    _run([cc, f"--offload-arch={ARCH}", "-O3", *common,
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-c", os.path.join(CSRC, "amk_decode.hip"), "-o", kobj], verbose)
     _run([cc, "-x", "c++", "-O2", "-fno-fast-math", "-ffp-contract=off", "-D__HIP_PLATFORM_AMD__",
           "-I/opt/rocm/include", *common,
           "-c", os.path.join(CSRC, "amk_host.cpp"), "-o", hobj], verbose)
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", tmp, "-lpthread"], verbose)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *kobjs, hobj, "-o", tmp, "-lpthread"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -102,6 +102,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ i32x4 ldbuf(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufCacheNT);
 }
+// Agent-coherent (sc1) 16-byte buffer load, for vectors written by other blocks in this launch.
+constexpr int kBufCacheSC1 = 16;
+__device__ __forceinline__ f32x4 ldbuf_c(__amdgpu_buffer_rsrc_t rs, int voff) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kBufCacheSC1);
+  return f32x4{__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z), __int_as_float(v.w)};
+}
 
 
 // ------------------------------------------------------------------------------------------
@@ -262,59 +268,76 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-constexpr int kMaxPairsPerThread = 8;  // vectors up to 2 * 8 * 512 = 8192 elements per pass
+constexpr int kNormQuads = 4;  // RMSNorm inputs up to 4 * 4 * 512 = 8192 elements
+constexpr int kVecQuads = 8;   // vector_to_lds issues up to 8 float4 loads per thread per pass
 
 // xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w), x from the coherent residual (or the bf16
-// embedding row for layer 0), zero padded to whole weight chunks.
+// embedding row for layer 0), zero padded to whole weight chunks. All loads of a thread are
+// issued before the first use, so the read costs one round trip.
 template <int FMT, bool FROM_EMBED>
 __device__ __forceinline__ void rmsnorm_to_lds(const KParams& p, const float* __restrict__ w, float* xs, float* red) {
 #pragma clang fp contract(off)
   const int H = p.H;
   const int tid = opaque(threadIdx.x);
-  float v[kMaxPairsPerThread][2];
+  f32x4 v[kNormQuads];
+  if (FROM_EMBED) {
+    const uint16_t* row = p.embed + static_cast<size_t>(p.token) * H;
 #pragma unroll
-  for (int k = 0; k < kMaxPairsPerThread; ++k) {
-    const int e = 2 * (tid + k * kThreads);
-    v[k][0] = v[k][1] = 0.f;
-    if (e < H) {
-      if (FROM_EMBED) {
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(p.embed + static_cast<size_t>(p.token) * H + e);
-        v[k][0] = bf_lo(static_cast<int>(b));
-        v[k][1] = bf_hi(static_cast<int>(b));
-      } else {
-        ldc2(p.x + e, v[k][0], v[k][1]);
+    for (int k = 0; k < kNormQuads; ++k) {
+      const int e = 4 * (tid + k * kThreads);
+      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (e < H) {
+        const uint2 b = *reinterpret_cast<const uint2*>(row + e);
+        v[k] = f32x4{bf_lo(static_cast<int>(b.x)), bf_hi(static_cast<int>(b.x)), bf_lo(static_cast<int>(b.y)),
+                     bf_hi(static_cast<int>(b.y))};
       }
     }
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.x, static_cast<uint32_t>(H) * 4u);
+#pragma unroll
+    for (int k = 0; k < kNormQuads; ++k) v[k] = ldbuf_c(rs, 16 * (tid + k * kThreads));  // zeros past H
   }
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxPairsPerThread; ++k) ss += v[k][0] * v[k][0] + v[k][1] * v[k][1];
+  for (int k = 0; k < kNormQuads; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   ss = block_sum(ss, red);
   const float ms = ss / static_cast<float>(H);
   const float r = 1.0f / sqrtf(ms + p.eps);
 #pragma unroll
-  for (int k = 0; k < kMaxPairsPerThread; ++k) {
-    const int e = 2 * (tid + k * kThreads);
+  for (int k = 0; k < kNormQuads; ++k) {
+    const int e = 4 * (tid + k * kThreads);
     if (e < H) {
-      xs[swz<FMT>(e)] = round_bf16((v[k][0] * r) * w[e]);
-      xs[swz<FMT>(e + 1)] = round_bf16((v[k][1] * r) * w[e + 1]);
+      const float4 wv = *reinterpret_cast<const float4*>(w + e);
+      f32x4 o;
+      o.x = round_bf16((v[k].x * r) * wv.x);
+      o.y = round_bf16((v[k].y * r) * wv.y);
+      o.z = round_bf16((v[k].z * r) * wv.z);
+      o.w = round_bf16((v[k].w * r) * wv.w);
+      *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = o;
     }
   }
   for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
   __syncthreads();
 }
 
-// xs <- coherent vector src[0..K) (already bf16-valued), zero padded.
+// xs <- coherent vector src[0..K) (already bf16-valued), zero padded to whole chunks. Four
+// consecutive elements land in one float4 of the swizzled layout (the lane's column count is a
+// multiple of 4); loads past K read zeros, which also fills the padding.
 template <int FMT>
 __device__ __forceinline__ void vector_to_lds(const float* src, int K, float* xs) {
   const int tid = opaque(threadIdx.x);
-  for (int e = 2 * tid; e < K; e += 2 * kThreads) {
-    float a, b;
-    ldc2(src + e, a, b);
-    xs[swz<FMT>(e)] = a;
-    xs[swz<FMT>(e + 1)] = b;
+  const int Kp = padded<FMT>(K);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<uint32_t>(K) * 4u);
+  for (int e0 = 0; e0 < Kp; e0 += 4 * kVecQuads * kThreads) {
+    f32x4 v[kVecQuads];
+#pragma unroll
+    for (int k = 0; k < kVecQuads; ++k) v[k] = ldbuf_c(rs, 4 * e0 + 16 * (tid + k * kThreads));
+#pragma unroll
+    for (int k = 0; k < kVecQuads; ++k) {
+      const int e = e0 + 4 * (tid + k * kThreads);
+      if (e < Kp) *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = v[k];
+    }
   }
-  for (int e = K + tid; e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
   __syncthreads();
 }
 

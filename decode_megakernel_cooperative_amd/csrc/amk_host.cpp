@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -15,6 +16,7 @@
 #include "amk_kparams.h"
 
 extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax);
+extern "C" __attribute__((visibility("hidden"))) const void* amk_stream_kernel_handle(int head_dim, int fmt, int gmax);
 extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle();
 
 namespace {
@@ -92,6 +94,8 @@ struct amk_model {
   int lds_bytes = 0;
   int gmax = 4;
   int s_cap = 1;
+  bool stream = true;       // streaming kernel (tagged hand-offs); false: grid-barrier kernel
+  uint32_t tag0 = 1;        // tag base of the next launch (streaming kernel)
   const void* kernel = nullptr;
   uint64_t spin_limit = kDefaultSpinLimit;
   uint64_t* trace = nullptr;
@@ -232,17 +236,49 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
 
   // grid / LDS / splits
   m->grid = prop.multiProcessorCount;
-  m->s_cap = std::max(1, m->grid / c.n_kv_heads);
   const int G = c.n_q_heads / c.n_kv_heads;
   m->gmax = G <= 4 ? 4 : 8;
+  {
+    const char* kv = std::getenv("AMK_KERNEL");
+    m->stream = !(kv && std::string(kv) == "barrier");
+  }
+  if (m->stream && m->gmax != 4) m->stream = false;  // the streaming kernel covers G <= 4
+  // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
+  // of one output on the lanes of a wave, so it takes at most 64
+  m->s_cap = std::max(1, m->grid / c.n_kv_heads);
+  if (m->stream) m->s_cap = std::min(m->s_cap, 64);
   const int cw = q8 ? 1024 : 512;
   auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
+  auto a4 = [](int64_t n) { return (n + 3) / 4 * 4; };
   const int64_t xs_f = std::max({pad(H), pad(QD), pad(F)});
-  const int64_t attn_f = std::max<int64_t>(static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2),
-                                           3 * static_cast<int64_t>(G) * m->s_cap + 2 * amk::kThreads);
-  m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
+  if (m->stream) {
+    const int64_t nb = m->grid;
+    auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+    const int64_t qkv_pairs = QKV / 2;
+    const int64_t maxpairs = std::max({cdiv(qkv_pairs, nb), cdiv(H / 2, nb), 2 * cdiv(F / 2, nb), cdiv(V / 2, nb)});
+    const int64_t waves = amk::kWaves;
+    const int64_t vec = a4(std::max(xs_f, G * hd + hd));
+    const int64_t part = a4(std::max(maxpairs * waves * 2, waves * G * (hd + 2)));
+    const int64_t scl_stride = a4(2 * maxpairs);
+    const int64_t xres = a4(2 * cdiv(H / 2, nb)), rope = a4(hd);
+    if (maxpairs > amk::kThreads) { delete m; return fail(AMK_ERR_UNSUPPORTED, "too many row pairs per block"); }
+    if (H > 8192 || F > 32768) { delete m; return fail(AMK_ERR_UNSUPPORTED, "hidden or ffn too large"); }
+    int64_t o = vec;
+    m->kp.lds_part = static_cast<int32_t>(o); o += part;
+    m->kp.lds_scl = static_cast<int32_t>(o); m->kp.lds_scl_stride = static_cast<int32_t>(scl_stride); o += 2 * scl_stride;
+    m->kp.lds_nw = 0;
+    m->kp.lds_xres = static_cast<int32_t>(o); o += xres;
+    m->kp.lds_rope = static_cast<int32_t>(o); o += rope;
+    if (V / 2 * nb >= (int64_t(1) << 31)) { delete m; return fail(AMK_ERR_UNSUPPORTED, "vocab too large for the block split"); }
+    m->lds_bytes = static_cast<int>(4 * o);
+    m->kernel = amk_stream_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
+  } else {
+    const int64_t attn_f = std::max<int64_t>(static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2),
+                                             3 * static_cast<int64_t>(G) * m->s_cap + 2 * amk::kThreads);
+    m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
+    m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
+  }
   if (m->lds_bytes > 160 * 1024) { delete m; return fail(AMK_ERR_UNSUPPORTED, "LDS need exceeds 160 KB"); }
-  m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
   if (!m->kernel) { delete m; return fail(AMK_ERR_UNSUPPORTED, "no kernel variant"); }
   he = hipFuncSetAttribute(m->kernel, hipFuncAttributeMaxDynamicSharedMemorySize, m->lds_bytes);
   if (he != hipSuccess) { delete m; return fail(AMK_ERR_HIP, std::string("hipFuncSetAttribute: ") + hipGetErrorString(he)); }
@@ -263,6 +299,12 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   const size_t s_bctr = stake(4 * amk::kCtrStride * amk::kBarrierCtrs);
   const size_t s_epoch = stake(4 * amk::kCtrStride);
   const size_t s_err = stake(4 * amk::kCtrStride);
+  // tagged exchange words of the streaming kernel (8 bytes each), one contiguous region
+  const size_t s_tag = so;
+  const size_t t_x = stake(8 * H), t_q = stake(8 * QD), t_kv = stake(8 * KD), t_o = stake(8 * QD / 2),
+               t_m = stake(8 * F / 2);
+  const size_t t_part = stake(8 * static_cast<size_t>(c.n_q_heads) * m->s_cap * (hd + 2));
+  const size_t s_tag_end = so;
   m->scratch_bytes = so;
 
   he = hipMalloc(&m->weights, m->weight_bytes);
@@ -405,6 +447,14 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   k.epoch = reinterpret_cast<unsigned*>(S + s_epoch);
   k.err = reinterpret_cast<unsigned*>(S + s_err);
   k.spin_limit = m->spin_limit;
+  k.tagged = reinterpret_cast<uint64_t*>(S + s_tag);
+  k.tagged_bytes = static_cast<uint32_t>(s_tag_end - s_tag);
+  k.tx = reinterpret_cast<uint64_t*>(S + t_x);
+  k.tq = reinterpret_cast<uint64_t*>(S + t_q);
+  k.tkv = reinterpret_cast<uint64_t*>(S + t_kv);
+  k.to = reinterpret_cast<uint64_t*>(S + t_o);
+  k.tm = reinterpret_cast<uint64_t*>(S + t_m);
+  k.tpart = reinterpret_cast<uint64_t*>(S + t_part);
   *out = m;
   return AMK_OK;
 }
@@ -427,6 +477,8 @@ int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, fl
   k.spin_limit = m->spin_limit;
   k.trace = m->trace;
   k.trace_stride = m->trace_stride;
+  k.tag0 = m->tag0;
+  m->tag0 += static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
   void* args[] = {&k};
   HIP_TRY(hipLaunchCooperativeKernel(m->kernel, dim3(m->grid), dim3(amk::kThreads), args,
                                      static_cast<unsigned>(m->lds_bytes), static_cast<hipStream_t>(stream)));
@@ -461,11 +513,16 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   info->grid_blocks = m->grid;
   info->block_threads = amk::kThreads;
   info->lds_bytes = m->lds_bytes;
-  info->barriers_per_step = amk::kStagesPerLayer * m->cfg.n_layers;
+  // grid-wide hand-offs per step: barriers (barrier kernel) or tagged vector exchanges
+  // (streaming kernel: RMSNorm input, q, split partials, attention output, RMSNorm input, SwiGLU
+  // output per layer, then the final RMSNorm input)
+  info->barriers_per_step = m->stream ? amk::kTagsPerLayer * m->cfg.n_layers + 1
+                                      : amk::kStagesPerLayer * m->cfg.n_layers;
   info->weight_bytes = static_cast<int64_t>(m->weight_bytes);
   info->scratch_bytes = static_cast<int64_t>(m->scratch_bytes);
   info->max_splits = m->s_cap;
   info->device = m->device;
+  info->kernel = m->stream ? AMK_KERNEL_STREAM : AMK_KERNEL_BARRIER;
   return AMK_OK;
 }
 
@@ -560,8 +617,8 @@ int amk_set_spin_limit(amk_model* m, uint64_t ticks) {
 
 int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block) {
   if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
-  if (trace && events_per_block < 2 + 2 * amk::kStagesPerLayer * m->cfg.n_layers)
-    return fail(AMK_ERR_INVALID_ARG, "events_per_block too small");
+  const int need = m->stream ? 3 + 11 * m->cfg.n_layers : 2 + 2 * amk::kStagesPerLayer * m->cfg.n_layers;
+  if (trace && events_per_block < need) return fail(AMK_ERR_INVALID_ARG, "events_per_block too small");
   m->trace = trace;
   m->trace_stride = trace ? events_per_block : 0;
   return AMK_OK;

@@ -10,6 +10,11 @@ constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line per counter
 constexpr int kBarrierCtrs = 8;        // arrival counters (block id mod 8)
 constexpr int kStagesPerLayer = 5;     // grid barriers per layer
 
+// Tags of the streaming kernel's exchange words: stage `which` of layer l in a launch writes tag
+// tag0 + l * kTagsPerLayer + which; the host advances tag0 by kTagsPerLayer * L + 1 per launch.
+constexpr int kTagsPerLayer = 6;
+enum { kTagQKV = 0, kTagPart = 1, kTagO = 2, kTagXO = 3, kTagM = 4, kTagXD = 5 };
+
 struct KParams {
   // model
   int32_t H, L, nq, nkv, hd, F, V, max_ctx;
@@ -48,7 +53,19 @@ struct KParams {
   unsigned* bctr;                           // barrier arrival counters (stride kCtrStride)
   unsigned* epoch;                          // barriers completed by earlier launches
   unsigned* err;                            // device error flag
-  uint64_t spin_limit;                      // wall-clock ticks per barrier wait
+  uint64_t spin_limit;                      // wall-clock ticks per barrier wait / poll
+  // streaming kernel: tagged exchange words (low 32 bits payload, high 32 bits tag), all inside
+  // one region so a single buffer resource covers them
+  uint64_t* tagged; uint32_t tagged_bytes;
+  uint64_t* tx;                             // [H] residual (fp32)
+  uint64_t* tq;                             // [nq*hd] rotated queries (fp32)
+  uint64_t* tkv;                            // [2][nkv][hd/2] K/V of pos, bf16 dims (i, i+hd/2)
+  uint64_t* tpart;                          // [nq][s_cap][hd+2] split partials: values, max, sum
+  uint64_t* to;                             // [nq*hd/2] attention output, 2 bf16 per word
+  uint64_t* tm;                             // [F/2] SwiGLU output, 2 bf16 per word
+  uint32_t tag0;
+  // streaming kernel: LDS layout (offsets in floats)
+  int32_t lds_part, lds_scl, lds_scl_stride, lds_nw, lds_xres, lds_rope;
   uint64_t* trace;                          // optional [grid][trace_stride] wall-clock stamps
   int32_t trace_stride;
 };

@@ -63,16 +63,25 @@ typedef struct {
 
 typedef struct amk_model amk_model; /* opaque, library-owned */
 
+/* Kernel a model runs: the streaming kernel (tagged hand-offs, weight ring; default for
+ * models with at most 4 query heads per kv head) or the grid-barrier kernel. The environment
+ * variable AMK_KERNEL=barrier at load time selects the barrier kernel. */
+#define AMK_KERNEL_BARRIER 0
+#define AMK_KERNEL_STREAM 1
+
 /* Launch geometry and memory of a loaded model (for tests and benchmarks). */
 typedef struct {
   int32_t grid_blocks;          /* persistent blocks (one per compute unit)                 */
   int32_t block_threads;        /* threads per block                                         */
   int32_t lds_bytes;            /* dynamic LDS per block                                     */
-  int32_t barriers_per_step;    /* grid barriers inside one decode step                      */
+  int32_t barriers_per_step;    /* grid-wide hand-offs in one decode step: grid barriers
+                                   (barrier kernel, 5 per layer) or tagged vector exchanges
+                                   (streaming kernel, 6 per layer + 1)                       */
   int64_t weight_bytes;         /* device bytes of packed weights + scales + norms           */
   int64_t scratch_bytes;        /* device bytes of library scratch                           */
   int32_t max_splits;           /* upper bound on KV splits per kv head                      */
   int32_t device;               /* HIP device the model lives on                             */
+  int32_t kernel;               /* AMK_KERNEL_STREAM or AMK_KERNEL_BARRIER                    */
 } amk_info;
 
 /* Copies, packs, (for AMK_W8A16) quantizes and uploads a model to the current device.
@@ -141,16 +150,20 @@ int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* cod
  * the current device and stores the mean microseconds per barrier in *us_out. Synchronous. */
 int amk_bench_barrier(int32_t iters, float* us_out);
 
-/* Debug control: bound (in 100 MHz wall-clock ticks) on any single grid-barrier wait;
- * 0 restores the default (one second). A tiny bound makes steps fail cleanly with
- * BARRIER_TIMEOUT, which is how the timeout path is exercised. */
+/* Debug control: bound (in 100 MHz wall-clock ticks) on any single grid-barrier wait or
+ * hand-off poll; 0 restores the default (one second). A tiny bound makes steps fail cleanly
+ * with BARRIER_TIMEOUT, which is how the timeout path is exercised. */
 int amk_set_spin_limit(amk_model* m, uint64_t ticks);
 
 /* Debug control: per-block stage timestamps. When trace is non-NULL, every later step of this
- * model writes, for each block b, the 100 MHz wall clock into trace[b * events_per_block + e]:
- * e = 0 at kernel entry, then the arrival and the exit of every grid barrier in order, then the
- * end of the lm_head stage. trace: device uint64 [grid_blocks][events_per_block], caller-owned;
- * events_per_block must be at least 2 + 2 * barriers_per_step. NULL switches tracing off.
+ * model writes, for each block b, the 100 MHz wall clock into trace[b * events_per_block + e].
+ * Barrier kernel: e = 0 at kernel entry, then the arrival and the exit of every grid barrier in
+ * order, then the end of the lm_head stage (at least 2 + 10 * n_layers events). Streaming
+ * kernel: e = 0 at entry, e = 1 when the first RMSNorm is in LDS, then per layer 11 events (QKV
+ * epilogue, q received, attention partial stored, split merge stored, attention output received,
+ * O epilogue, RMSNorm 2 in LDS, gate/up epilogue, SwiGLU output received, down epilogue, next
+ * RMSNorm in LDS), then the end of the lm_head epilogue (at least 3 + 11 * n_layers events).
+ * trace: device uint64 [grid_blocks][events_per_block], caller-owned. NULL switches tracing off.
  * Errors: INVALID_ARG for a null handle or a too small events_per_block. */
 int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block);
 
