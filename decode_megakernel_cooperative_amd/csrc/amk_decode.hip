@@ -80,6 +80,15 @@ __device__ __forceinline__ void stc(unsigned* p, unsigned v) {
 __device__ __forceinline__ void stc16(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Tagged exchange word: payload in the low 32 bits, the tag of the stage that wrote it in the
+// high 32 bits. A 64-bit aligned store is single-copy atomic, so a payload is never seen with
+// another stage's tag.
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t payload, uint32_t tag) {
+  __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_payload(const uint64_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+}
 
 // An empty asm that hides a value from the optimizer. Stage functions start from an opaque
 // copy of the thread index so the compiler recomputes their (cheap) per-thread addresses
@@ -163,6 +172,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += xor_lane<32>(v);
   return v;
 }
+// max / sum over each aligned group of SP lanes (SP a power of two <= 64, wave-uniform), in
+// every lane of the group
+__device__ __forceinline__ float seg_sum(float v, int SP) {
+  if (SP >= 2) v += dpp<0xB1>(v);
+  if (SP >= 4) v += dpp<0x4E>(v);
+  if (SP >= 8) v += dpp<0x141>(v);
+  if (SP >= 16) v += dpp<0x140>(v);
+  if (SP >= 32) v += xor_lane<16>(v);
+  if (SP >= 64) v += xor_lane<32>(v);
+  return v;
+}
+__device__ __forceinline__ float seg_max(float v, int SP) {
+  if (SP >= 2) v = fmaxf(v, dpp<0xB1>(v));
+  if (SP >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if (SP >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if (SP >= 16) v = fmaxf(v, dpp<0x140>(v));
+  if (SP >= 32) v = fmaxf(v, xor_lane<16>(v));
+  if (SP >= 64) v = fmaxf(v, xor_lane<32>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0xB1>(v));
   v = fmaxf(v, dpp<0x4E>(v));
@@ -256,89 +286,180 @@ __device__ __forceinline__ int padded(int K) {
   return (K + CW - 1) / CW * CW;
 }
 
+// Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt 0): weight loads in
+// flight stay in flight across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum(v);
   if (lane == 0) red[wave] = v;
-  __syncthreads();
+  wg_barrier();
   float t = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t += red[w];
-  __syncthreads();
+  wg_barrier();
   return t;
 }
 
-constexpr int kNormQuads = 4;  // RMSNorm inputs up to 4 * 4 * 512 = 8192 elements
-constexpr int kVecQuads = 8;   // vector_to_lds issues up to 8 float4 loads per thread per pass
+__device__ __forceinline__ uint32_t tag_of(const KParams& p, int layer, int which) {
+  return p.tag0 + static_cast<uint32_t>(layer * kTagsPerLayer + which);
+}
+// byte offset of a tagged buffer inside the tagged region
+__device__ __forceinline__ int toff(const KParams& p, const uint64_t* buf) {
+  return static_cast<int>(reinterpret_cast<const uint8_t*>(buf) - reinterpret_cast<const uint8_t*>(p.tagged));
+}
 
-// xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w), x from the coherent residual (or the bf16
-// embedding row for layer 0), zero padded to whole weight chunks. All loads of a thread are
-// issued before the first use, so the read costs one round trip.
-template <int FMT, bool FROM_EMBED>
-__device__ __forceinline__ void rmsnorm_to_lds(const KParams& p, const float* __restrict__ w, float* xs, float* red) {
-#pragma clang fp contract(off)
-  const int H = p.H;
+// Block-wide poll of nquads 16-byte quads (two tagged words each) of the tagged region: thread t
+// owns quads t + 512 b, b < VB (then further batches). When both tags of every quad of a thread
+// equal `tag` on the first read (the common case once the producers are done) visit(b, qi,
+// payload0, payload1) runs straight away; otherwise the thread re-reads its pending quads until
+// they are fresh. off(qi) is the quad's byte offset, or kOOB for a quad to skip. Returns false if
+// the step must be abandoned (timeout, or an error raised elsewhere).
+template <int VB, class Off, class Visit>
+__device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_t tag, Off off, Visit visit) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.tagged, p.tagged_bytes);
   const int tid = opaque(threadIdx.x);
-  f32x4 v[kNormQuads];
-  if (FROM_EMBED) {
-    const uint16_t* row = p.embed + static_cast<size_t>(p.token) * H;
+  for (int q0 = 0; q0 < nquads; q0 += kThreads * VB) {
+    i32x4 v[VB];
+    uint32_t skip = 0;
 #pragma unroll
-    for (int k = 0; k < kNormQuads; ++k) {
-      const int e = 4 * (tid + k * kThreads);
-      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (e < H) {
-        const uint2 b = *reinterpret_cast<const uint2*>(row + e);
-        v[k] = f32x4{bf_lo(static_cast<int>(b.x)), bf_hi(static_cast<int>(b.x)), bf_lo(static_cast<int>(b.y)),
-                     bf_hi(static_cast<int>(b.y))};
+    for (int b = 0; b < VB; ++b) {
+      const int qi = q0 + b * kThreads + tid;
+      const int o = qi < nquads ? off(qi) : kOOB;
+      skip |= (o == kOOB) ? (1u << b) : 0u;
+      v[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, kBufCacheSC1);
+    }
+    auto pending = [&]() {
+      uint32_t pend = 0;
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        const bool good = ((skip >> b) & 1u) ||
+                          (static_cast<uint32_t>(v[b].y) == tag && static_cast<uint32_t>(v[b].w) == tag);
+        pend |= good ? 0u : (1u << b);
+      }
+      return pend;
+    };
+    uint32_t pend = pending();
+    if (pend != 0u) {
+      const uint64_t t_start = wall_clock64();
+      unsigned it = 0;
+      while (pend != 0u) {
+        if (((++it) & 15u) == 0) {
+          if (ldc(p.err) != 0u || wall_clock64() - t_start > p.spin_limit) {
+            stc(p.err, 1u);
+            return false;
+          }
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int b = 0; b < VB; ++b)
+          if (pend & (1u << b))
+            v[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(q0 + b * kThreads + tid), 0, kBufCacheSC1);
+        pend = pending();
       }
     }
-  } else {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.x, static_cast<uint32_t>(H) * 4u);
 #pragma unroll
-    for (int k = 0; k < kNormQuads; ++k) v[k] = ldbuf_c(rs, 16 * (tid + k * kThreads));  // zeros past H
+    for (int b = 0; b < VB; ++b)
+      if (!((skip >> b) & 1u))
+        visit(b, q0 + b * kThreads + tid, static_cast<uint32_t>(v[b].x), static_cast<uint32_t>(v[b].z));
+  }
+  return true;
+}
+
+constexpr int kNormVB = 8;  // RMSNorm inputs up to 2 * 8 * 512 = 8192 elements
+
+// xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w) for the first layer, x = the bf16 embedding row,
+// zero padded to whole weight chunks.
+template <int FMT>
+__device__ __forceinline__ void rmsnorm_embed_to_lds(const KParams& p, const float* __restrict__ w, float* xs,
+                                                     float* red) {
+#pragma clang fp contract(off)
+  const int H = p.H, tid = opaque(threadIdx.x);
+  const uint16_t* row = p.embed + static_cast<size_t>(p.token) * H;
+  float2 xv[kNormVB], wv[kNormVB];
+#pragma unroll
+  for (int b = 0; b < kNormVB; ++b) {
+    const int e = 2 * (b * kThreads + tid);
+    xv[b] = float2{0.f, 0.f};
+    wv[b] = float2{0.f, 0.f};
+    if (e < H) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(row + e);
+      xv[b] = float2{bf_lo(static_cast<int>(u)), bf_hi(static_cast<int>(u))};
+      wv[b] = *reinterpret_cast<const float2*>(w + e);
+    }
   }
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kNormQuads; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+  for (int b = 0; b < kNormVB; ++b) ss += xv[b].x * xv[b].x + xv[b].y * xv[b].y;
   ss = block_sum(ss, red);
-  const float ms = ss / static_cast<float>(H);
-  const float r = 1.0f / sqrtf(ms + p.eps);
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + p.eps);
 #pragma unroll
-  for (int k = 0; k < kNormQuads; ++k) {
-    const int e = 4 * (tid + k * kThreads);
+  for (int b = 0; b < kNormVB; ++b) {
+    const int e = 2 * (b * kThreads + tid);
     if (e < H) {
-      const float4 wv = *reinterpret_cast<const float4*>(w + e);
-      f32x4 o;
-      o.x = round_bf16((v[k].x * r) * wv.x);
-      o.y = round_bf16((v[k].y * r) * wv.y);
-      o.z = round_bf16((v[k].z * r) * wv.z);
-      o.w = round_bf16((v[k].w * r) * wv.w);
-      *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = o;
+      xs[swz<FMT>(e)] = round_bf16((xv[b].x * r) * wv[b].x);
+      xs[swz<FMT>(e + 1)] = round_bf16((xv[b].y * r) * wv[b].y);
     }
   }
   for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
-  __syncthreads();
 }
 
-// xs <- coherent vector src[0..K) (already bf16-valued), zero padded to whole chunks. Four
-// consecutive elements land in one float4 of the swizzled layout (the lane's column count is a
-// multiple of 4); loads past K read zeros, which also fills the padding.
+// xs <- RMSNorm of the residual x polled from its tagged words (tag `tag`), zero padded. The
+// weights are loaded with the poll, in the same round trip. Returns false if abandoned.
 template <int FMT>
-__device__ __forceinline__ void vector_to_lds(const float* src, int K, float* xs) {
-  const int tid = opaque(threadIdx.x);
-  const int Kp = padded<FMT>(K);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, static_cast<uint32_t>(K) * 4u);
-  for (int e0 = 0; e0 < Kp; e0 += 4 * kVecQuads * kThreads) {
-    f32x4 v[kVecQuads];
+__device__ __forceinline__ bool norm_from_x(const KParams& p, const float* __restrict__ w, uint32_t tag, float* xs,
+                                            float* red) {
+#pragma clang fp contract(off)
+  const int H = p.H, tid = opaque(threadIdx.x);
+  float2 xv[kNormVB], wv[kNormVB];
 #pragma unroll
-    for (int k = 0; k < kVecQuads; ++k) v[k] = ldbuf_c(rs, 4 * e0 + 16 * (tid + k * kThreads));
+  for (int b = 0; b < kNormVB; ++b) {
+    const int e = 2 * (b * kThreads + tid);
+    wv[b] = e < H ? *reinterpret_cast<const float2*>(w + e) : float2{0.f, 0.f};
+    xv[b] = float2{0.f, 0.f};
+  }
+  const int ob = toff(p, p.tx);
+  const bool ok = poll_block<kNormVB>(p, H / 2, tag, [&](int qi) { return ob + 16 * qi; },
+                                      [&](int b, int, uint32_t a, uint32_t c) {
+                                        xv[b] = float2{__uint_as_float(a), __uint_as_float(c)};
+                                      });
+  float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < kVecQuads; ++k) {
-      const int e = e0 + 4 * (tid + k * kThreads);
-      if (e < Kp) *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = v[k];
+  for (int b = 0; b < kNormVB; ++b) ss += xv[b].x * xv[b].x + xv[b].y * xv[b].y;
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + p.eps);
+#pragma unroll
+  for (int b = 0; b < kNormVB; ++b) {
+    const int e = 2 * (b * kThreads + tid);
+    if (e < H) {
+      xs[swz<FMT>(e)] = round_bf16((xv[b].x * r) * wv[b].x);
+      xs[swz<FMT>(e + 1)] = round_bf16((xv[b].y * r) * wv[b].y);
     }
   }
-  __syncthreads();
+  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  return ok;
+}
+
+// xs <- a bf16 vector of K elements polled from its tagged words (two bf16 per word), zero
+// padded. Four consecutive elements land in one float4 of the swizzled layout.
+template <int FMT>
+__device__ __forceinline__ bool vector_from_words(const KParams& p, const uint64_t* src, int K, uint32_t tag,
+                                                  float* xs) {
+  const int ob = toff(p, src);
+  const bool ok = poll_block<8>(p, K / 4, tag, [&](int qi) { return ob + 16 * qi; },
+                                [&](int, int qi, uint32_t a, uint32_t c) {
+                                  *reinterpret_cast<f32x4*>(xs + swz<FMT>(4 * qi)) =
+                                      f32x4{bf16_to_f32(a & 0xffffu), bf16_to_f32(a >> 16), bf16_to_f32(c & 0xffffu),
+                                            bf16_to_f32(c >> 16)};
+                                });
+  for (int e = K + opaque(threadIdx.x); e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  return ok;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -368,15 +489,18 @@ struct GemvPlan {
   int pa, pb;
 };
 
+// Pairs are split over the waves in units of `unit` pairs (2 for gate/up, so a wave's SwiGLU
+// outputs fill whole two-value exchange words).
 template <int FMT>
-__device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave) {
+__device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave, int unit) {
   GemvPlan g;
   g.RB = K * Fmt<FMT>::WB;
   g.nch = (g.RB + 1023) >> 10;
   g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
   const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
-  g.pa = static_cast<int>((static_cast<int64_t>(npairs) * gw) / NW);
-  g.pb = static_cast<int>((static_cast<int64_t>(npairs) * (gw + 1)) / NW);
+  const int nu = npairs / unit;
+  g.pa = unit * static_cast<int>((static_cast<int64_t>(nu) * gw) / NW);
+  g.pb = unit * static_cast<int>((static_cast<int64_t>(nu) * (gw + 1)) / NW);
   return g;
 }
 
@@ -433,7 +557,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   if (row < 2 * pb) {
     if (FMT == 1) A = Sc[row];
     if (EPI == EPI_RESID) {
-      B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(p.token) * p.H + row]) : ldc(p.x + row);
+      B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(p.token) * p.H + row]) : ld_payload(p.tx + row);
     } else if (EPI == EPI_QKV) {
       const int half = p.hd >> 1;
       const int i = (row >> 1) % half;
@@ -442,36 +566,46 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   }
 }
 
+// Runs in lane 0 for one finished row pair: scale (applied by the caller), then q / K / V with
+// RoPE (and the K/V append to the cache), the residual add, SwiGLU, or the logits. Values that
+// cross blocks are written as tagged words (tag tg). SwiGLU outputs pair up: an even pair keeps
+// its value in mprev and the following odd pair writes both.
 template <int EPI>
-__device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1) {
+__device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1,
+                                         uint32_t tg, float& mprev) {
 #pragma clang fp contract(off)
   if (EPI == EPI_QKV) {
     const int half = p.hd >> 1;
     const int hb = pr / half, i = pr - hb * half;
+    float a = y0, b = y1;
     if (hb < p.nq + p.nkv) {
       const float c = b0, s = b1;
-      const float a = y0 * c - y1 * s;
-      const float b = y1 * c + y0 * s;
-      if (hb < p.nq) {
-        stc(p.q + hb * p.hd + i, a);
-        stc(p.q + hb * p.hd + i + half, b);
-      } else {
-        uint16_t* kp = p.kv + ((static_cast<size_t>(layer) * 2 * p.nkv + (hb - p.nq)) * p.max_ctx + p.pos) * p.hd;
-        stc16(kp + i, f32_to_bf16(a));
-        stc16(kp + i + half, f32_to_bf16(b));
-      }
+      a = y0 * c - y1 * s;
+      b = y1 * c + y0 * s;
+    }
+    if (hb < p.nq) {
+      st_tag(p.tq + hb * p.hd + i, __float_as_uint(a), tg);
+      st_tag(p.tq + hb * p.hd + i + half, __float_as_uint(b), tg);
     } else {
-      const int g = hb - p.nq - p.nkv;
-      uint16_t* vp = p.kv + ((static_cast<size_t>(layer * 2 + 1) * p.nkv + g) * p.max_ctx + p.pos) * p.hd;
-      stc16(vp + i, f32_to_bf16(y0));
-      stc16(vp + i + half, f32_to_bf16(y1));
+      const int kvs = hb < p.nq + p.nkv ? 0 : 1;
+      const int g = hb - p.nq - kvs * p.nkv;
+      const uint16_t ba = f32_to_bf16(a), bb = f32_to_bf16(b);
+      uint16_t* dst = p.kv + ((static_cast<size_t>(layer * 2 + kvs) * p.nkv + g) * p.max_ctx + p.pos) * p.hd;
+      dst[i] = ba;
+      dst[i + half] = bb;
+      st_tag(p.tkv + (kvs * p.nkv + g) * half + i, static_cast<uint32_t>(ba) | (static_cast<uint32_t>(bb) << 16), tg);
     }
   } else if (EPI == EPI_RESID) {
-    stc(p.x + 2 * pr, b0 + y0);
-    stc(p.x + 2 * pr + 1, b1 + y1);
+    st_tag(p.tx + 2 * pr, __float_as_uint(b0 + y0), tg);
+    st_tag(p.tx + 2 * pr + 1, __float_as_uint(b1 + y1), tg);
   } else if (EPI == EPI_SWIGLU) {
-    const float sg = y0 / (1.0f + expf(-y0));
-    stc(p.m + pr, round_bf16(sg * y1));
+    const float m = (y0 / (1.0f + expf(-y0))) * y1;
+    if ((pr & 1) == 0) {
+      mprev = m;
+    } else {
+      st_tag(p.tm + (pr >> 1), static_cast<uint32_t>(f32_to_bf16(mprev)) | (static_cast<uint32_t>(f32_to_bf16(m)) << 16),
+             tg);
+    }
   } else {
     p.logits[2 * pr] = y0;
     p.logits[2 * pr + 1] = y1;
@@ -501,7 +635,8 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const Gemv
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
                                              const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
-                                             float wA, float wB, Cursor& c, float& acc0, float& acc1) {
+                                             float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
+                                             float& mprev) {
   constexpr int CW = Fmt<FMT>::CW;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
@@ -519,7 +654,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
-      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1);
+      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1, tg, mprev);
     }
     c.advance(g.cpp);
   }
@@ -542,7 +677,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
                                               GemvRegs& R) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), EPI == EPI_SWIGLU ? 2 : 1);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, AMK_PREFETCH_ITEMS > 1, R);
 }
@@ -553,8 +688,9 @@ __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* _
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __restrict__ W,
                                          const float* __restrict__ Sc, int K, int npairs, const float* xs,
-                                         int layer, bool rfe, GemvRegs& R) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+                                         int layer, bool rfe, GemvRegs& R, uint32_t tg) {
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), EPI == EPI_SWIGLU ? 2 : 1);
+  float mprev = 0.f;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   const float* xlane = xs + __lane_id() * 4;
   for (int base = g.pa; base < g.pb; base += kSeg) {
@@ -570,9 +706,9 @@ __device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __rest
     }
     float acc0 = 0.f, acc1 = 0.f;
     for (int it = 0; it < items; it += 2) {
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
       gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
       gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
     }
   }
@@ -649,7 +785,7 @@ __device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, 
 }
 
 template <int HD, int GMAX>
-__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, int* flag, AttnRegs<GMAX>& R) {
+__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, AttnRegs<GMAX>& R) {
   constexpr int kAttnU = AttnRegs<GMAX>::U;
   constexpr int LPP = HD / 8;     // lanes per position (8 bf16 = 16 bytes per lane)
   constexpr int PPW = 64 / LPP;   // positions per wave load
@@ -659,6 +795,8 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
   const int li = lane % LPP, ri = lane / LPP, d0 = li * 8;
   float* wp = smem;  // [kWaves][GMAX][HD + 2]
+  const float* qs = smem + kWaves * GMAX * (HD + 2);                 // q of the G heads [G][HD]
+  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(qs + G * HD);  // K(pos) [HD], V(pos) [HD]
   const AttnUnit a = attn_unit<HD>(p);
   const int g = a.g, j = a.j;
 
@@ -671,23 +809,24 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     i32x4 (&KB)[kAttnU] = R.kb;
     i32x4 (&VB)[kAttnU] = R.vb;
     const int step = kWaves * kAttnU;
-    // the current position was left out of the prefetch (it was being written): load it now,
-    // branch free (lanes of other positions read out of range and keep their data)
+    // the current position was left out of the prefetch (this step's QKV stage writes it): take
+    // it from LDS, where the unit that holds pos received it with q
+    if (t0 <= p.pos && p.pos < t1) {  // uniform
+      const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + li * 8);
+      const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + li * 8);
 #pragma unroll
-    for (int uu = 0; uu < kAttnU; ++uu) {
+      for (int uu = 0; uu < kAttnU; ++uu) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int gg = wave + b * step + uu * kWaves;
-        const int t = t0 + gg * PPW + ri;
-        const bool here = gg < ngroups && t == p.pos;
-        const int voff = here ? t * (HD * 2) + li * 16 : kOOB;
-        const i32x4 k = ldbuf(kb, voff, 0), v = ldbuf(vb, voff, 0);
-        if (b == 0) {
-          KA[uu] = here ? k : KA[uu];
-          VA[uu] = here ? v : VA[uu];
-        } else {
-          KB[uu] = here ? k : KB[uu];
-          VB[uu] = here ? v : VB[uu];
+        for (int b = 0; b < 2; ++b) {
+          const int gg = wave + b * step + uu * kWaves;
+          const bool here = gg < ngroups && t0 + gg * PPW + ri == p.pos;
+          if (b == 0) {
+            KA[uu] = here ? kl : KA[uu];
+            VA[uu] = here ? vl : VA[uu];
+          } else {
+            KB[uu] = here ? kl : KB[uu];
+            VB[uu] = here ? vl : VB[uu];
+          }
         }
       }
     }
@@ -699,9 +838,9 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h < G) {
-        const float* qp = p.q + (g * G + h) * HD + d0;
+        const float* qp = qs + h * HD + d0;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) ldc2(qp + i, qv[h][i], qv[h][i + 1]);
+        for (int i = 0; i < 8; ++i) qv[h][i] = qp[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) qv[h][i] = 0.f;
@@ -803,10 +942,11 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       }
     }
   }
-  __syncthreads();
+  wg_barrier();
   if (!a.active) return;
 
-  // merge the waves of the block -> this unit's partial
+  // merge the waves of the block -> this unit's partial (values, max, sum) as tagged words
+  const uint32_t tpart = tag_of(p, layer, kTagPart);
   for (int t = tid; t < G * HD; t += kThreads) {
     const int h = t / HD, d = t - h * HD;
     float M = NEG_INF;
@@ -821,174 +961,216 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       A += src[d] * e;
       Lsum += src[HD + 1] * e;
     }
-    const size_t slot = static_cast<size_t>(g * G + h) * p.s_cap + j;
-    stc(p.pacc + slot * HD + d, A);
+    uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
+    st_tag(dst + d, __float_as_uint(A), tpart);
     if (d == 0) {
-      stc(p.pml + slot * 2, M);
-      stc(p.pml + slot * 2 + 1, Lsum);
+      st_tag(dst + HD, __float_as_uint(M), tpart);
+      st_tag(dst + HD + 1, __float_as_uint(Lsum), tpart);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(p.gctr + g * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old == static_cast<unsigned>(S - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*flag == 0) return;
+}
 
-  // last block of this kv head: merge the S split partials of its G heads
-  if (tid == 0) stc(p.gctr + g * kCtrStride, 0u);
-  // threads own (head, dim pair) items and, RW ways, the splits; their partial sums are loaded
-  // first so they travel together with the split maxima and sums
-  const int items = G * (HD / 2);
-  int RW = 1;
-  while (RW * 2 * items <= kThreads) RW *= 2;
-  constexpr int kBatch = 16;
-  const int it = tid % items, r = tid / items;
-  const int hh = it / (HD / 2), dd = 2 * (it - hh * (HD / 2));
-  const size_t hbase = static_cast<size_t>(g * G + hh) * p.s_cap;
-  float v0[kBatch], v1[kBatch];
+// The blocks of kv head g each merge one slice of the head's G * HD outputs over its S splits
+// (log-sum-exp weights) and write it as tagged bf16 pairs. Thread t holds split t % SP of output
+// word w0 + t / SP (plus 512 / SP in the second round); SP = S rounded up to a power of two.
+template <int HD>
+__device__ __forceinline__ bool attention_merge_slice(const KParams& p, int layer) {
+  const float NEG_INF = -__builtin_inff();
+  const AttnUnit a = attn_unit<HD>(p);
+  if (!a.active) return true;
+  const int G = p.nq / p.nkv, S = p.S, g = a.g, j = a.j;
+  const int tid = opaque(threadIdx.x);
+  const int nw = G * HD / 2;  // output words of the kv head (2 bf16 each)
+  const int w0 = nw * j / S, w1 = nw * (j + 1) / S;
+  int SP = 1;
+  while (SP < S) SP *= 2;
+  const int wpr = kThreads / SP;  // words per round
+  const int obase = toff(p, p.tpart);
+  float av[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float mv[2] = {NEG_INF, NEG_INF}, lv[2] = {0.f, 0.f};
+  const bool ok = poll_block<4>(
+      p, 4 * kThreads, tag_of(p, layer, kTagPart),
+      [&](int qi) {
+        const int bq = qi / kThreads, t = qi - bq * kThreads;
+        const int r = bq >> 1, which = bq & 1;
+        const int wd = w0 + r * wpr + t / SP, sp = t % SP;
+        if (wd >= w1 || sp >= S) return kOOB;
+        const int h = wd / (HD / 2), d = 2 * (wd - h * (HD / 2));
+        const int rec = (g * G + h) * p.s_cap + sp;
+        return obase + (rec * (HD + 2) + (which ? HD : d)) * 8;
+      },
+      [&](int bq, int, uint32_t x0, uint32_t x1) {
+        if (bq & 1) {
+          mv[bq >> 1] = __uint_as_float(x0);
+          lv[bq >> 1] = __uint_as_float(x1);
+        } else {
+          av[bq >> 1][0] = __uint_as_float(x0);
+          av[bq >> 1][1] = __uint_as_float(x1);
+        }
+      });
+  const uint32_t to_tag = tag_of(p, layer, kTagO);
 #pragma unroll
-  for (int b = 0; b < kBatch; ++b) {
-    const int jj = r + b * RW;
-    v0[b] = v1[b] = 0.f;
-    if (r < RW && jj < S) ldc2(p.pacc + (hbase + jj) * HD + dd, v0[b], v1[b]);
-  }
-  // one wave per head turns the split maxima / sums into merge weights e^(m_j - M) / L
-  float* wts = smem;                 // [G][S]
-  float* part = smem + G * S;        // [RW][items][2]
-  if (wave < G) {
-    const size_t base = static_cast<size_t>(g * G + wave) * p.s_cap;
-    float M = NEG_INF;
-    for (int jj = lane; jj < S; jj += 64) M = fmaxf(M, ldc(p.pml + (base + jj) * 2));
-    M = wave_max(M);
-    float Lsum = 0.f;
-    for (int jj = lane; jj < S; jj += 64) {
-      float mj, lj;
-      ldc2(p.pml + (base + jj) * 2, mj, lj);
-      const float e = (mj == NEG_INF) ? 0.f : __expf(mj - M);
-      wts[wave * S + jj] = e;
-      Lsum += lj * e;
+  for (int r = 0; r < 2; ++r) {
+    const int wd = w0 + r * wpr + tid / SP, sp = tid % SP;
+    const bool v = wd < w1 && sp < S;
+    const float mj = v ? mv[r] : NEG_INF;
+    const float M = seg_max(mj, SP);
+    const float e = (mj == NEG_INF) ? 0.f : __expf(mj - M);
+    const float Ls = seg_sum(v ? lv[r] * e : 0.f, SP);
+    const float wgt = e * (1.0f / Ls);
+    const float o0 = seg_sum(v ? av[r][0] * wgt : 0.f, SP);
+    const float o1 = seg_sum(v ? av[r][1] * wgt : 0.f, SP);
+    if (ok && v && sp == 0) {
+      const int h = wd / (HD / 2), d = 2 * (wd - h * (HD / 2));
+      st_tag(p.to + ((g * G + h) * HD + d) / 2,
+             static_cast<uint32_t>(f32_to_bf16(o0)) | (static_cast<uint32_t>(f32_to_bf16(o1)) << 16), to_tag);
     }
-    Lsum = wave_sum(Lsum);
-    const float inv = 1.0f / Lsum;
-    for (int jj = lane; jj < S; jj += 64) wts[wave * S + jj] *= inv;
   }
-  __syncthreads();
-  if (r < RW) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int jj = r + b * RW;
-      if (jj < S) {
-        a0 += v0[b] * wts[hh * S + jj];
-        a1 += v1[b] * wts[hh * S + jj];
-      }
-    }
-    for (int jb = r + kBatch * RW; jb < S; jb += RW) {  // only when S > kBatch * RW
-      float x0, x1;
-      ldc2(p.pacc + (hbase + jb) * HD + dd, x0, x1);
-      a0 += x0 * wts[hh * S + jb];
-      a1 += x1 * wts[hh * S + jb];
-    }
-    part[(r * items + it) * 2] = a0;
-    part[(r * items + it) * 2 + 1] = a1;
-  }
-  __syncthreads();
-  for (int i2 = tid; i2 < items; i2 += kThreads) {
-    float a0 = 0.f, a1 = 0.f;
-    for (int rr = 0; rr < RW; ++rr) {
-      a0 += part[(rr * items + i2) * 2];
-      a1 += part[(rr * items + i2) * 2 + 1];
-    }
-    const int h = i2 / (HD / 2), d = 2 * (i2 - h * (HD / 2));
-    stc(p.o + (g * G + h) * HD + d, round_bf16(a0));
-    stc(p.o + (g * G + h) * HD + d + 1, round_bf16(a1));
-  }
+  return ok;
 }
 
 // ------------------------------------------------------------------------------------------
 // the persistent decode kernel
 // ------------------------------------------------------------------------------------------
+// q of the unit's G heads (fp32) into qs[G][HD] and, for the unit that holds pos, K/V(pos)
+// (bf16 pairs of dims i, i + HD/2) into the bf16 area after it. Returns false if abandoned.
+template <int HD>
+__device__ __forceinline__ bool poll_q_kv(const KParams& p, int layer, float* qs) {
+  const AttnUnit a = attn_unit<HD>(p);
+  if (!a.active) return true;
+  constexpr int half = HD / 2;
+  const int G = p.nq / p.nkv;
+  const bool has_pos = a.t1 == p.pos + 1;
+  const int nq4 = G * HD / 2, nkv4 = has_pos ? half / 2 : 0;
+  const int oq = toff(p, p.tq) + a.g * G * HD * 8, ok_ = toff(p, p.tkv) + a.g * half * 8,
+            ov = toff(p, p.tkv) + (p.nkv + a.g) * half * 8;
+  uint16_t* kvp = reinterpret_cast<uint16_t*>(qs + G * HD);
+  return poll_block<2>(
+      p, nq4 + 2 * nkv4, tag_of(p, layer, kTagQKV),
+      [&](int qi) {
+        return qi < nq4 ? oq + 16 * qi : (qi < nq4 + nkv4 ? ok_ + 16 * (qi - nq4) : ov + 16 * (qi - nq4 - nkv4));
+      },
+      [&](int, int qi, uint32_t x0, uint32_t x1) {
+        if (qi < nq4) {
+          qs[2 * qi] = __uint_as_float(x0);
+          qs[2 * qi + 1] = __uint_as_float(x1);
+        } else {
+          const int r = qi - nq4;
+          const int kvs = r < nkv4 ? 0 : 1;
+          const int i = 2 * (r - kvs * nkv4);
+          uint16_t* d = kvp + kvs * HD;
+          d[i] = static_cast<uint16_t>(x0 & 0xffffu);
+          d[i + half] = static_cast<uint16_t>(x0 >> 16);
+          d[i + 1] = static_cast<uint16_t>(x1 & 0xffffu);
+          d[i + 1 + half] = static_cast<uint16_t>(x1 >> 16);
+        }
+      });
+}
+
 template <int HD, int FMT, int GMAX>
 __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float red[kWaves];
-  __shared__ int abort_flag, unit_flag;
+  __shared__ int abort_flag;
   if (threadIdx.x == 0) abort_flag = 0;
   const unsigned err0 = ldc(p.err);
-  const unsigned base = ldc(p.epoch);
   __syncthreads();
   if (err0 != 0u) return;
-  GridBarrier bar{p.bctr, base, 0u, p.spin_limit, p.err,
-                  p.trace ? p.trace + static_cast<size_t>(blockIdx.x) * p.trace_stride : nullptr, 0};
-  bar.stamp();
-  float* xs = smem;
+  uint64_t* trace = p.trace ? p.trace + static_cast<size_t>(blockIdx.x) * p.trace_stride : nullptr;
+  int ev = 0;
+  auto stamp = [&]() {
+    if (trace != nullptr && threadIdx.x == 0) trace[ev] = wall_clock64();
+    ++ev;
+  };
+  stamp();
+  float* xs = smem;                                  // GEMV input vector (swizzled)
+  float* qs = smem + kWaves * GMAX * (HD + 2);       // attention: q, K/V(pos)
+  const int H = p.H, L = p.L;
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;
   GemvRegs R;
   AttnRegs<GMAX> AR;
+  bool ok = true;
+  // end of a hand-off: the next stage's input is in LDS, or every thread leaves
+  auto handoff_done = [&]() -> bool {
+    if (!ok) abort_flag = 1;
+    wg_barrier();
+    if (abort_flag != 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      return false;
+    }
+    return true;
+  };
 
-  gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv, p.s_qkv, p.H, qkv_pairs, false, R);
-  for (int l = 0; l < p.L; ++l) {
-    // RMSNorm -> QKV GEMV -> RoPE, KV append
-    if (l == 0) rmsnorm_to_lds<FMT, true>(p, p.norm_in, xs, red);
-    else rmsnorm_to_lds<FMT, false>(p, p.norm_in + static_cast<size_t>(l) * p.H, xs, red);
-    if (AMK_FINE_TRACE) bar.stamp();
-    gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, p.H, qkv_pairs, xs, l, false, R);
-    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
-    bar.arrive();
+  gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv, p.s_qkv, H, qkv_pairs, false, R);
+  rmsnorm_embed_to_lds<FMT>(p, p.norm_in, xs, red);
+  stamp();
+  wg_barrier();
+  for (int l = 0; l < L; ++l) {
+    if (l > 0) {  // RMSNorm of the residual written by the previous layer's down stage
+      ok = norm_from_x<FMT>(p, p.norm_in + static_cast<size_t>(l) * H, tag_of(p, l - 1, kTagXD), xs, red);
+      stamp();
+      if (!handoff_done()) return;
+    }
+    // QKV GEMV -> RoPE; q, K/V(pos) as tagged words, K/V(pos) also into the cache
+    gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
+                           tag_of(p, l, kTagQKV));
     attention_prefetch<HD, GMAX>(p, l, AR);
-    if (!bar.wait(&abort_flag)) return;
+    wg_barrier();  // every wave is done with xs
+    stamp();
+    ok = poll_q_kv<HD>(p, l, qs);
+    stamp();
+    if (!handoff_done()) return;
 
-    // split-KV attention (+ merge by the last block of each kv head); the O-projection weights
-    // stream in meanwhile (they depend on nothing)
-    if (AMK_EARLY_WO)
-      gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, l == 0, R);
-    attention_stage<HD, GMAX>(p, l, smem, &unit_flag, AR);
-    bar.arrive();
-    if (!AMK_EARLY_WO)
-      gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, l == 0, R);
-    if (!bar.wait(&abort_flag)) return;
+    // split-KV attention -> the unit's partial; the kv head's blocks merge one slice each
+    attention_stage<HD, GMAX>(p, l, smem, AR);
+    stamp();
+    ok = attention_merge_slice<HD>(p, l);
+    stamp();
+    gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, l == 0, R);
+    wg_barrier();  // attention is done with LDS
+    if (ok) ok = vector_from_words<FMT>(p, p.to, qdim, tag_of(p, l, kTagO), xs);
+    stamp();
+    if (!handoff_done()) return;
 
     // O-projection + residual
-    vector_to_lds<FMT>(p.o, qdim, xs);
-    if (AMK_FINE_TRACE) bar.stamp();
-    gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, p.H / 2, xs, l, l == 0, R);
-    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
-    bar.arrive();
-    gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, p.H, p.F, false, R);
-    if (!bar.wait(&abort_flag)) return;
+    gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, xs, l, l == 0, R,
+                             tag_of(p, l, kTagXO));
+    gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, false, R);
+    wg_barrier();
+    stamp();
+    ok = norm_from_x<FMT>(p, p.norm_post + static_cast<size_t>(l) * H, tag_of(p, l, kTagXO), xs, red);
+    stamp();
+    if (!handoff_done()) return;
 
-    // RMSNorm -> gate/up GEMV -> SwiGLU
-    rmsnorm_to_lds<FMT, false>(p, p.norm_post + static_cast<size_t>(l) * p.H, xs, red);
-    if (AMK_FINE_TRACE) bar.stamp();
-    gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, p.H, p.F, xs, l, false, R);
-    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
-    bar.arrive();
-    gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, p.H / 2, false, R);
-    if (!bar.wait(&abort_flag)) return;
+    // gate/up GEMV -> SwiGLU
+    gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, xs, l, false, R,
+                              tag_of(p, l, kTagM));
+    gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
+    wg_barrier();
+    stamp();
+    ok = vector_from_words<FMT>(p, p.tm, p.F, tag_of(p, l, kTagM), xs);
+    stamp();
+    if (!handoff_done()) return;
 
     // down GEMV + residual
-    vector_to_lds<FMT>(p.m, p.F, xs);
-    if (AMK_FINE_TRACE) bar.stamp();
-    gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, p.H / 2, xs, l, false, R);
-    if (AMK_FINE_TRACE) { __syncthreads(); bar.stamp(); }
-    bar.arrive();
-    if (l + 1 < p.L)
-      gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, p.H, qkv_pairs,
+    gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, xs, l, false, R,
+                             tag_of(p, l, kTagXD));
+    if (l + 1 < L)
+      gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);
     else
-      gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, p.H, p.V / 2, false, R);
-    if (!bar.wait(&abort_flag)) return;
+      gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
+    wg_barrier();
+    stamp();
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) stc(p.epoch, base + bar.n);
   // final RMSNorm -> lm_head
-  rmsnorm_to_lds<FMT, false>(p, p.norm_final, xs, red);
-  gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, p.H, p.V / 2, xs, p.L, false, R);
-  __syncthreads();
-  bar.stamp();
+  ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
+  stamp();
+  if (!handoff_done()) return;
+  gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
+  wg_barrier();
+  stamp();
 }
 
 // barrier microbenchmark: `iters` grid barriers in one persistent launch

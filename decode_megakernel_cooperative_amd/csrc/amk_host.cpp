@@ -245,8 +245,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   if (m->stream && m->gmax != 4) m->stream = false;  // the streaming kernel covers G <= 4
   // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
   // of one output on the lanes of a wave, so it takes at most 64
-  m->s_cap = std::max(1, m->grid / c.n_kv_heads);
-  if (m->stream) m->s_cap = std::min(m->s_cap, 64);
+  m->s_cap = std::min(64, std::max(1, m->grid / c.n_kv_heads));
   const int cw = q8 ? 1024 : 512;
   auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
   auto a4 = [](int64_t n) { return (n + 3) / 4 * 4; };
@@ -273,8 +272,8 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     m->lds_bytes = static_cast<int>(4 * o);
     m->kernel = amk_stream_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
   } else {
-    const int64_t attn_f = std::max<int64_t>(static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2),
-                                             3 * static_cast<int64_t>(G) * m->s_cap + 2 * amk::kThreads);
+    // attention: the waves' softmax states, then q of the G heads and K/V(pos)
+    const int64_t attn_f = static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2) + G * hd + hd;
     m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
     m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
   }
@@ -516,8 +515,7 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   // grid-wide hand-offs per step: barriers (barrier kernel) or tagged vector exchanges
   // (streaming kernel: RMSNorm input, q, split partials, attention output, RMSNorm input, SwiGLU
   // output per layer, then the final RMSNorm input)
-  info->barriers_per_step = m->stream ? amk::kTagsPerLayer * m->cfg.n_layers + 1
-                                      : amk::kStagesPerLayer * m->cfg.n_layers;
+  info->barriers_per_step = amk::kTagsPerLayer * m->cfg.n_layers + 1;
   info->weight_bytes = static_cast<int64_t>(m->weight_bytes);
   info->scratch_bytes = static_cast<int64_t>(m->scratch_bytes);
   info->max_splits = m->s_cap;
@@ -617,7 +615,7 @@ int amk_set_spin_limit(amk_model* m, uint64_t ticks) {
 
 int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block) {
   if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
-  const int need = m->stream ? 3 + 11 * m->cfg.n_layers : 2 + 2 * amk::kStagesPerLayer * m->cfg.n_layers;
+  const int need = 3 + 11 * m->cfg.n_layers;
   if (trace && events_per_block < need) return fail(AMK_ERR_INVALID_ARG, "events_per_block too small");
   m->trace = trace;
   m->trace_stride = trace ? events_per_block : 0;

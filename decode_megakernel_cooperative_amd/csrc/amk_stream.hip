@@ -67,6 +67,9 @@ constexpr int kSC1 = 16;  // buffer load cache policy: agent coherent (tagged wo
 #ifndef AMK_DEFER
 #define AMK_DEFER 0       // 1: a stage's last ring round defers its refills to the next hand-off
 #endif
+#ifndef AMK_ATT_PF
+#define AMK_ATT_PF 0      // attention items per wave prefetched into registers during QKV
+#endif
 #ifndef AMK_DBG
 #define AMK_DBG 0         // 1: per-stage debug stamps after the stage stamps (compute end, B exit)
 #endif
@@ -239,6 +242,7 @@ struct Stage {
   int C;         // the block's item count
   int nch, rb, pb0, np;  // GEMV
   int t0, t1, g;         // attention
+  int pf0;               // attention: first item (items pf0 .. c0 - 1 come from the prefetch registers)
 };
 
 // Fills the per-block stage tables (threads 0..47: type = tid / 8, wave = tid % 8).
@@ -278,8 +282,13 @@ __device__ __forceinline__ void build_tables(const KParams& p, int4* stab, int4*
   }
   if (w == 0) stab[type] = st;
   const int c0 = C * w / kWaves, c1 = C * (w + 1) / kWaves;
-  const int pl = c0 / nch;
-  wtab[type * kWaves + w] = int4{c0, c1, (pl << 16) | (c0 - pl * nch), (c1 - c0 + RING - 1) / RING};
+  if (type == ST_ATT) {  // the first AMK_ATT_PF items come from the prefetch registers
+    const int r0 = min(c1, c0 + AMK_ATT_PF);
+    wtab[type * kWaves + w] = int4{r0, c1, c0, (c1 - r0 + RING - 1) / RING};
+  } else {
+    const int pl = c0 / nch;
+    wtab[type * kWaves + w] = int4{c0, c1, (pl << 16) | (c0 - pl * nch), (c1 - c0 + RING - 1) / RING};
+  }
 }
 
 // Stage k of the program as seen by wave w.
@@ -290,7 +299,7 @@ __device__ __forceinline__ Stage stage_at(const KParams& p, const Lds& L, int k,
   s.layer = k < nst ? k / kProgStages : p.L;
   s.type = k < nst ? k - s.layer * kProgStages : (k == nst ? ST_LM : ST_END);
   s.nch = 1; s.rb = 0; s.pb0 = 0; s.np = 0; s.C = 0; s.t0 = 0; s.t1 = 0; s.g = 0;
-  s.c0 = s.c1 = s.pl0 = s.ch0 = s.rounds = 0;
+  s.c0 = s.c1 = s.pl0 = s.ch0 = s.rounds = s.pf0 = 0;
   if (s.type == ST_END) return s;
   const int4 a = L.stab[s.type];
   const int4 x = L.wtab[s.type * kWaves + w];
@@ -302,7 +311,9 @@ __device__ __forceinline__ Stage stage_at(const KParams& p, const Lds& L, int k,
   }
   s.c0 = uni(x.x); s.c1 = uni(x.y);
   const int pc = uni(x.z);
-  s.pl0 = pc >> 16; s.ch0 = pc & 0xffff;
+  s.pf0 = pc;
+  s.pl0 = s.type == ST_ATT ? 0 : pc >> 16;
+  s.ch0 = s.type == ST_ATT ? 0 : pc & 0xffff;
   s.rounds = uni(x.w);
   return s;
 }
@@ -391,6 +402,31 @@ struct IssueCursor {
   }
 };
 
+// Issues wave w's first AMK_ATT_PF attention items of layer `layer` (K and V of PPC positions
+// each) into dedicated registers; they stream in during the QKV stage.
+template <int HD, int NA, int NR>
+__device__ __forceinline__ void att_prefetch(const KParams& p, const Lds& L, int layer, int w, i32x4 (&pk)[NR],
+                                             i32x4 (&pv)[NR]) {
+  constexpr int LPP = HD / 8, PPC = 64 / LPP;
+  const Stage s = stage_at(p, L, layer * kProgStages + ST_ATT, w);
+  const int lane = __lane_id();
+  const size_t blk = static_cast<size_t>(p.max_ctx) * HD;
+  const uint16_t* kb = p.kv + (static_cast<size_t>(layer * 2) * p.nkv + s.g) * blk;
+  const uint16_t* vb = p.kv + (static_cast<size_t>(layer * 2 + 1) * p.nkv + s.g) * blk;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, static_cast<uint32_t>(blk * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, static_cast<uint32_t>(blk * 2));
+  static_for<0, NA>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const int c = s.pf0 + i;
+    const int tb = s.t0 + c * PPC;
+    const int t = tb + lane / LPP;
+    const int voff = (c < s.c0 && t < s.t1) ? (lane / LPP) * (HD * 2) + (lane % LPP) * 16 : kOOB;
+    const int soff = uni(c < s.c0 ? tb * (HD * 2) : 0);
+    pk[i] = ldnt(rk, voff, soff);
+    pv[i] = ldnt(rv, voff, soff);
+  });
+}
+
 // ------------------------------------------------------------------------------------------
 // ring: consume side
 // ------------------------------------------------------------------------------------------
@@ -466,8 +502,12 @@ __device__ __forceinline__ void att_consume(const KParams& p, const Lds& L, int 
     vf[2 * d + 1] = bf_hi(vr[d]);
   }
   const float NEG_INF = -__builtin_inff();
+  float sc[GMAX], mn[GMAX];
+  bool moved = false;
 #pragma unroll
   for (int h = 0; h < GMAX; ++h) {
+    sc[h] = NEG_INF;
+    mn[h] = st.m[h];
     if (h < G) {
       const float* qp = L.vec + h * HD + li * 8;
       const f32x4 q0 = *reinterpret_cast<const f32x4*>(qp);
@@ -478,14 +518,33 @@ __device__ __forceinline__ void att_consume(const KParams& p, const Lds& L, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) dot = __builtin_fmaf(q1[i], kf[4 + i], dot);
       dot = group_sum<LPP>(dot);
-      const float sc = valid ? dot * p.attn_scale : NEG_INF;
-      const float mn = fmaxf(st.m[h], sc);
-      const float corr = (st.m[h] == NEG_INF) ? 0.f : __expf(st.m[h] - mn);
-      const float pe = (sc == NEG_INF) ? 0.f : __expf(sc - mn);
+      sc[h] = valid ? dot * p.attn_scale : NEG_INF;
+      mn[h] = fmaxf(st.m[h], sc[h]);
+      moved |= mn[h] != st.m[h];
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(moved) == 0) {
+    // no running maximum of the wave moved: no rescale
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < G) {
+        const float pe = (sc[h] == NEG_INF) ? 0.f : __expf(sc[h] - st.m[h]);
+        st.l[h] += pe;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[h][i] = __builtin_fmaf(pe, vf[i], st.acc[h][i]);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+      const float corr = (st.m[h] == NEG_INF) ? 0.f : __expf(st.m[h] - mn[h]);
+      const float pe = (sc[h] == NEG_INF) ? 0.f : __expf(sc[h] - mn[h]);
       st.l[h] = st.l[h] * corr + pe;
 #pragma unroll
       for (int i = 0; i < 8; ++i) st.acc[h][i] = __builtin_fmaf(pe, vf[i], st.acc[h][i] * corr);
-      st.m[h] = mn;
+      st.m[h] = mn[h];
     }
   }
 }
@@ -862,6 +921,8 @@ __global__ void __launch_bounds__(kThreads, 1) amk_stream_kernel(const KParams p
   IssueCursor<HD, RING> ic;
   ic.enter(p, L, 0, w);
   static_for<0, RING>([&](auto si) { ic.issue(p, L, w, ra[si.value], rb[si.value]); });
+  i32x4 pk[AMK_ATT_PF > 0 ? AMK_ATT_PF : 1], pv[AMK_ATT_PF > 0 ? AMK_ATT_PF : 1];  // next attention items
+  if (AMK_ATT_PF > 0) att_prefetch<HD, AMK_ATT_PF>(p, L, 0, w, pk, pv);
   bool ring_free = false;
   // Deferred refills, issued behind a hand-off's poll: the workgroup barrier makes every wave's
   // poll loads enter the unit's (in-order) memory queue before any refill does.
@@ -879,6 +940,10 @@ __global__ void __launch_bounds__(kThreads, 1) amk_stream_kernel(const KParams p
     if (st.type == ST_ATT) {
       AttnState<GMAX> as;
       att_reset<GMAX>(as);
+      static_for<0, AMK_ATT_PF>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        if (st.pf0 + i < st.c0) att_consume<HD, GMAX>(p, L, st.t0, st.t1, st.pf0 + i, pk[i], pv[i], as);
+      });
       run_stage<HD, FMT, GMAX, RING, true>(p, L, st, w, ra, rb, ic, as, ring_free);
       att_finish<HD, GMAX>(p, L, w, as);
     } else {
@@ -1056,6 +1121,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_stream_kernel(const KParams p
       stamp();
       // input of the next GEMV: RMSNorm of the new residual (gate/up, next layer's QKV, lm_head)
       ok = norm_from_x<FMT>(p, L, tg, nwv, refill, pdbg);
+      if (AMK_ATT_PF > 0 && !is_o && l + 1 < p.L) att_prefetch<HD, AMK_ATT_PF>(p, L, l + 1, w, pk, pv);
       const Stage sn = stage_at(p, L, k + 1, w);
       if (FMT == 1) scn = load_scales(stage_s(p, sn.type, sn.layer) + 2 * sn.pb0, sn.np, sn.type == ST_GU);
       stamp();

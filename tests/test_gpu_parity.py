@@ -116,8 +116,7 @@ def test_invalid_arguments_rejected():
     torch.cuda.synchronize()
     dec.sync()
     info = dec.info()
-    per_layer = 6 * shape.n_layers + 1 if info.kernel == D.amk.AMK_KERNEL_STREAM else 5 * shape.n_layers
-    assert info.grid_blocks >= 1 and info.barriers_per_step == per_layer
+    assert info.grid_blocks >= 1 and info.barriers_per_step == 6 * shape.n_layers + 1
     assert D.amk_kv_cache_bytes(dec.model) == dec.kv.numel() * 2
     dec.close()
 
