@@ -47,6 +47,9 @@
 #ifndef AMK_PREFETCH_ITEMS
 #define AMK_PREFETCH_ITEMS 2  // GEMV items issued before the barrier in front of a stage (1 or 2)
 #endif
+#ifndef AMK_EARLY_KV
+#define AMK_EARLY_KV 0    // 1: issue the attention K/V prefetch before the QKV GEMV instead of after it
+#endif
 #ifndef AMK_EARLY_WO
 #define AMK_EARLY_WO 0    // 1: issue the O-projection prefetch at the start of attention
 #endif
@@ -85,6 +88,12 @@ __device__ __forceinline__ void stc16(uint16_t* p, uint16_t v) {
 // another stage's tag.
 __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t payload, uint32_t tag) {
   __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 32-bit exchange word for a bf16 value: the value in the high half, the low 16 bits of the tag
+// in the low half (single-copy atomic as well).
+__device__ __forceinline__ void st_tag16(uint32_t* p, uint16_t value, uint32_t tag) {
+  __hip_atomic_store(p, (static_cast<uint32_t>(value) << 16) | (tag & 0xffffu), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_payload(const uint64_t* p) {
   return __uint_as_float(static_cast<uint32_t>(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
@@ -372,6 +381,69 @@ __device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_
   return true;
 }
 
+// Block-wide poll of bf16 values in 32-bit tagged words (value << 16 | tag & 0xffff) into the
+// GEMV input vector, zero padded: thread t owns quads t + 512 b (four words = four consecutive
+// elements, one float4 of the swizzled layout). Returns false if abandoned.
+template <int FMT>
+__device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint32_t* src, int K, uint32_t tag,
+                                                    float* xs) {
+  constexpr int VB = 8;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.tagged, p.tagged_bytes);
+  const int tid = opaque(threadIdx.x);
+  const int ob = static_cast<int>(reinterpret_cast<const uint8_t*>(src) - reinterpret_cast<const uint8_t*>(p.tagged));
+  const uint32_t t16 = tag & 0xffffu;
+  const int nq = K / 4;
+  for (int q0 = 0; q0 < nq; q0 += kThreads * VB) {
+    i32x4 v[VB];
+#pragma unroll
+    for (int b = 0; b < VB; ++b) {
+      const int qi = q0 + b * kThreads + tid;
+      v[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, qi < nq ? ob + 16 * qi : kOOB, 0, kBufCacheSC1);
+    }
+    auto pending = [&]() {
+      uint32_t pend = 0;
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        const int qi = q0 + b * kThreads + tid;
+        const bool good = qi >= nq || (((static_cast<uint32_t>(v[b].x) & 0xffffu) == t16) &&
+                                       ((static_cast<uint32_t>(v[b].y) & 0xffffu) == t16) &&
+                                       ((static_cast<uint32_t>(v[b].z) & 0xffffu) == t16) &&
+                                       ((static_cast<uint32_t>(v[b].w) & 0xffffu) == t16));
+        pend |= good ? 0u : (1u << b);
+      }
+      return pend;
+    };
+    uint32_t pend = pending();
+    if (pend != 0u) {
+      const uint64_t t_start = wall_clock64();
+      unsigned it = 0;
+      while (pend != 0u) {
+        if (((++it) & 15u) == 0) {
+          if (ldc(p.err) != 0u || wall_clock64() - t_start > p.spin_limit) {
+            stc(p.err, 1u);
+            return false;
+          }
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int b = 0; b < VB; ++b)
+          if (pend & (1u << b))
+            v[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, ob + 16 * (q0 + b * kThreads + tid), 0, kBufCacheSC1);
+        pend = pending();
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < VB; ++b) {
+      const int qi = q0 + b * kThreads + tid;
+      if (qi < nq)
+        *reinterpret_cast<f32x4*>(xs + swz<FMT>(4 * qi)) =
+            f32x4{bf_hi(v[b].x), bf_hi(v[b].y), bf_hi(v[b].z), bf_hi(v[b].w)};
+    }
+  }
+  for (int e = K + tid; e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  return true;
+}
+
 constexpr int kNormVB = 8;  // RMSNorm inputs up to 2 * 8 * 512 = 8192 elements
 
 // xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w) for the first layer, x = the bf16 embedding row,
@@ -568,8 +640,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
 
 // Runs in lane 0 for one finished row pair: scale (applied by the caller), then q / K / V with
 // RoPE (and the K/V append to the cache), the residual add, SwiGLU, or the logits. Values that
-// cross blocks are written as tagged words (tag tg). SwiGLU outputs pair up: an even pair keeps
-// its value in mprev and the following odd pair writes both.
+// cross blocks are written as tagged words (tag tg); a SwiGLU output is one 32-bit word.
 template <int EPI>
 __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1,
                                          uint32_t tg, float& mprev) {
@@ -600,12 +671,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
     st_tag(p.tx + 2 * pr + 1, __float_as_uint(b1 + y1), tg);
   } else if (EPI == EPI_SWIGLU) {
     const float m = (y0 / (1.0f + expf(-y0))) * y1;
-    if ((pr & 1) == 0) {
-      mprev = m;
-    } else {
-      st_tag(p.tm + (pr >> 1), static_cast<uint32_t>(f32_to_bf16(mprev)) | (static_cast<uint32_t>(f32_to_bf16(m)) << 16),
-             tg);
-    }
+    st_tag16(reinterpret_cast<uint32_t*>(p.tm) + pr, f32_to_bf16(m), tg);
+    (void)mprev;
   } else {
     p.logits[2 * pr] = y0;
     p.logits[2 * pr + 1] = y1;
@@ -677,7 +744,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
                                               GemvRegs& R) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), EPI == EPI_SWIGLU ? 2 : 1);
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), 1);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, AMK_PREFETCH_ITEMS > 1, R);
 }
@@ -689,7 +756,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __restrict__ W,
                                          const float* __restrict__ Sc, int K, int npairs, const float* xs,
                                          int layer, bool rfe, GemvRegs& R, uint32_t tg) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), EPI == EPI_SWIGLU ? 2 : 1);
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), 1);
   float mprev = 0.f;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   const float* xlane = xs + __lane_id() * 4;
@@ -861,6 +928,11 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       for (int uu = 0; uu < kAttnU; ++uu) {
         const int gg = gbase + uu * kWaves;
         const bool valid = gg < ngroups && (t0 + gg * PPW + ri) < t1;
+        if (gg >= ngroups) {  // uniform: no position of this group is in the unit
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h) s[uu][h] = NEG_INF;
+          continue;
+        }
         float kf[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -889,6 +961,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) {
+          if (gbase + uu * kWaves >= ngroups) continue;  // uniform
           const float pe = (s[uu][h] == NEG_INF) ? 0.f : __expf(s[uu][h] - mnew);
           lr[h] += pe;
 #pragma unroll
@@ -905,7 +978,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     for (int gb = wave; gb < ngroups; gb += 2 * step) {
       compute(gb, KA, VA);
       load(gb + 2 * step, KA, VA);
-      compute(gb + step, KB, VB);
+      if (gb + step < ngroups) compute(gb + step, KB, VB);  // uniform
       load(gb + 3 * step, KB, VB);
     }
 
@@ -1113,9 +1186,10 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
       if (!handoff_done()) return;
     }
     // QKV GEMV -> RoPE; q, K/V(pos) as tagged words, K/V(pos) also into the cache
+    if (AMK_EARLY_KV) attention_prefetch<HD, GMAX>(p, l, AR);
     gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
                            tag_of(p, l, kTagQKV));
-    attention_prefetch<HD, GMAX>(p, l, AR);
+    if (!AMK_EARLY_KV) attention_prefetch<HD, GMAX>(p, l, AR);
     wg_barrier();  // every wave is done with xs
     stamp();
     ok = poll_q_kv<HD>(p, l, qs);
@@ -1149,7 +1223,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
     wg_barrier();
     stamp();
-    ok = vector_from_words<FMT>(p, p.tm, p.F, tag_of(p, l, kTagM), xs);
+    ok = vector_from_words16<FMT>(p, reinterpret_cast<const uint32_t*>(p.tm), p.F, tag_of(p, l, kTagM), xs);
     stamp();
     if (!handoff_done()) return;
 
