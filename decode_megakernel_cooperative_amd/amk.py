@@ -25,8 +25,8 @@ AMK_ERR_BARRIER_TIMEOUT = -5
 AMK_ERR_OOM = -6
 AMK_BF16 = 0
 AMK_W8A16 = 1
-AMK_KERNEL_BARRIER = 0
-AMK_KERNEL_STREAM = 1
+AMK_KERNEL_WAVE = 0
+AMK_KERNEL_BLOCK = 1
 
 EXPORTED = ("amk_load_weights", "amk_decode_step", "amk_sync", "amk_kv_cache_bytes", "amk_get_info",
             "amk_export_quantized", "amk_quantize_int8", "amk_bench_barrier", "amk_set_spin_limit",
@@ -49,7 +49,7 @@ class amk_config(ctypes.Structure):
 
 class amk_info(ctypes.Structure):
     _fields_ = [("grid_blocks", ctypes.c_int32), ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("barriers_per_step", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
+                ("handoffs_per_step", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("scratch_bytes", ctypes.c_int64), ("max_splits", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("kernel", ctypes.c_int32)]
 

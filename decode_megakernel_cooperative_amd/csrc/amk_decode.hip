@@ -876,27 +876,24 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     i32x4 (&KB)[kAttnU] = R.kb;
     i32x4 (&VB)[kAttnU] = R.vb;
     const int step = kWaves * kAttnU;
-    // the current position was left out of the prefetch (this step's QKV stage writes it): take
-    // it from LDS, where the unit that holds pos received it with q
-    if (t0 <= p.pos && p.pos < t1) {  // uniform
-      const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + li * 8);
-      const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + li * 8);
+    // The current position's K/V are written by this step's QKV stage on another block: plain
+    // stores that need not be visible here yet. The unit that holds pos received them with q
+    // (LDS); whatever the cache load of that slot returned is replaced before use.
+    const int gpos = (t0 <= p.pos && p.pos < t1) ? (p.pos - t0) / PPW : -1;  // uniform
+    const int rpos = (p.pos - t0) % PPW;
+    auto patch_pos = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
+      const int dg = gpos - gbase;
+      if (dg >= 0 && dg < kAttnU * kWaves && dg % kWaves == 0) {  // uniform: at most once per unit
+        const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + li * 8);
+        const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + li * 8);
 #pragma unroll
-      for (int uu = 0; uu < kAttnU; ++uu) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int gg = wave + b * step + uu * kWaves;
-          const bool here = gg < ngroups && t0 + gg * PPW + ri == p.pos;
-          if (b == 0) {
-            KA[uu] = here ? kl : KA[uu];
-            VA[uu] = here ? vl : VA[uu];
-          } else {
-            KB[uu] = here ? kl : KB[uu];
-            VB[uu] = here ? vl : VB[uu];
-          }
+        for (int uu = 0; uu < kAttnU; ++uu) {
+          const bool here = uu == dg / kWaves && ri == rpos;
+          kr[uu] = here ? kl : kr[uu];
+          vr[uu] = here ? vl : vr[uu];
         }
       }
-    }
+    };
     auto load = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
       attn_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
     };
@@ -976,9 +973,13 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
 
     // two buffers in flight; loads past the unit read zeros, so the loop body has no branch
     for (int gb = wave; gb < ngroups; gb += 2 * step) {
+      patch_pos(gb, KA, VA);
       compute(gb, KA, VA);
       load(gb + 2 * step, KA, VA);
-      if (gb + step < ngroups) compute(gb + step, KB, VB);  // uniform
+      if (gb + step < ngroups) {  // uniform
+        patch_pos(gb + step, KB, VB);
+        compute(gb + step, KB, VB);
+      }
       load(gb + 3 * step, KB, VB);
     }
 

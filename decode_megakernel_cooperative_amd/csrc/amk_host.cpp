@@ -94,7 +94,7 @@ struct amk_model {
   int lds_bytes = 0;
   int gmax = 4;
   int s_cap = 1;
-  bool stream = true;       // streaming kernel (tagged hand-offs); false: grid-barrier kernel
+  bool stream = false;      // true: block-split kernel (amk_stream.hip); false: wave-row kernel
   uint32_t tag0 = 1;        // tag base of the next launch (streaming kernel)
   const void* kernel = nullptr;
   uint64_t spin_limit = kDefaultSpinLimit;
@@ -240,9 +240,9 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   m->gmax = G <= 4 ? 4 : 8;
   {
     const char* kv = std::getenv("AMK_KERNEL");
-    m->stream = !(kv && std::string(kv) == "barrier");
+    m->stream = kv && std::string(kv) == "block";
   }
-  if (m->stream && m->gmax != 4) m->stream = false;  // the streaming kernel covers G <= 4
+  if (m->stream && m->gmax != 4) m->stream = false;  // the block-split kernel covers G <= 4
   // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
   // of one output on the lanes of a wave, so it takes at most 64
   m->s_cap = std::min(64, std::max(1, m->grid / c.n_kv_heads));
@@ -515,12 +515,12 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   // grid-wide hand-offs per step: barriers (barrier kernel) or tagged vector exchanges
   // (streaming kernel: RMSNorm input, q, split partials, attention output, RMSNorm input, SwiGLU
   // output per layer, then the final RMSNorm input)
-  info->barriers_per_step = amk::kTagsPerLayer * m->cfg.n_layers + 1;
+  info->handoffs_per_step = amk::kTagsPerLayer * m->cfg.n_layers + 1;
   info->weight_bytes = static_cast<int64_t>(m->weight_bytes);
   info->scratch_bytes = static_cast<int64_t>(m->scratch_bytes);
   info->max_splits = m->s_cap;
   info->device = m->device;
-  info->kernel = m->stream ? AMK_KERNEL_STREAM : AMK_KERNEL_BARRIER;
+  info->kernel = m->stream ? AMK_KERNEL_BLOCK : AMK_KERNEL_WAVE;
   return AMK_OK;
 }
 

@@ -63,25 +63,29 @@ typedef struct {
 
 typedef struct amk_model amk_model; /* opaque, library-owned */
 
-/* Kernel a model runs: the streaming kernel (tagged hand-offs, weight ring; default for
- * models with at most 4 query heads per kv head) or the grid-barrier kernel. The environment
- * variable AMK_KERNEL=barrier at load time selects the barrier kernel. */
-#define AMK_KERNEL_BARRIER 0
-#define AMK_KERNEL_STREAM 1
+/* Kernel a model runs. Both are one persistent cooperative launch per token with the same
+ * tagged hand-offs between stages; they differ in how a block splits a GEMV stage:
+ *   AMK_KERNEL_WAVE  (default): every wave owns whole output-row pairs and finishes them on its
+ *                    own (register window per wave, per-wave epilogue);
+ *   AMK_KERNEL_BLOCK: a block's 8 waves split the K axis of the block's rows (register weight
+ *                    ring, block-wide epilogue through LDS); only for models with at most 4
+ *                    query heads per kv head, selected with the environment variable
+ *                    AMK_KERNEL=block at load time. */
+#define AMK_KERNEL_WAVE 0
+#define AMK_KERNEL_BLOCK 1
 
 /* Launch geometry and memory of a loaded model (for tests and benchmarks). */
 typedef struct {
   int32_t grid_blocks;          /* persistent blocks (one per compute unit)                 */
   int32_t block_threads;        /* threads per block                                         */
   int32_t lds_bytes;            /* dynamic LDS per block                                     */
-  int32_t barriers_per_step;    /* grid-wide hand-offs in one decode step: grid barriers
-                                   (barrier kernel, 5 per layer) or tagged vector exchanges
-                                   (streaming kernel, 6 per layer + 1)                       */
+  int32_t handoffs_per_step;    /* grid-wide tagged vector exchanges in one decode step
+                                   (6 per layer + 1); the launch has no grid barrier        */
   int64_t weight_bytes;         /* device bytes of packed weights + scales + norms           */
   int64_t scratch_bytes;        /* device bytes of library scratch                           */
   int32_t max_splits;           /* upper bound on KV splits per kv head                      */
   int32_t device;               /* HIP device the model lives on                             */
-  int32_t kernel;               /* AMK_KERNEL_STREAM or AMK_KERNEL_BARRIER                    */
+  int32_t kernel;               /* AMK_KERNEL_WAVE or AMK_KERNEL_BLOCK                       */
 } amk_info;
 
 /* Copies, packs, (for AMK_W8A16) quantizes and uploads a model to the current device.

@@ -80,6 +80,22 @@ def test_g3_hd64_long_prefill_w8a16():
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+def test_long_split_current_position_late_in_unit(fmt):
+    """8 kv heads and a 12000-position prefilled cache: with one split per block each KV split
+    spans hundreds of positions, so the current position (written by this step's QKV stage on
+    another block) lies far past the positions a block loads before its q arrives. Its K/V must
+    come from the hand-off, not from the cache slot being written concurrently."""
+    shape = W.ModelShape("hd128-kv8-long", 512, 2, 16, 8, 128, 1024, 1000, False, 500000.0)
+    dec, orc, kv = build(shape, fmt, 12010, 12000, seed0=9)
+    info = dec.info()
+    log(f"  grid {info.grid_blocks}, max splits {info.max_splits}")
+    tok = W.gen_tokens(shape, 1, seed0=9)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 12000, [], 6, first_token=tok, check_kv=True)
+    _assert_gates(res, f"hd128-kv8-long fmt{fmt}")
+    dec.close()
+
+
 def test_determinism_and_idempotence():
     """No float atomics: repeated identical steps give bitwise-identical logits and KV entries."""
     wl = W.WORKLOADS["smollm2-135m-w8a16"]
@@ -116,7 +132,7 @@ def test_invalid_arguments_rejected():
     torch.cuda.synchronize()
     dec.sync()
     info = dec.info()
-    assert info.grid_blocks >= 1 and info.barriers_per_step == 6 * shape.n_layers + 1
+    assert info.grid_blocks >= 1 and info.handoffs_per_step == 6 * shape.n_layers + 1
     assert D.amk_kv_cache_bytes(dec.model) == dec.kv.numel() * 2
     dec.close()
 
