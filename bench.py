@@ -17,8 +17,10 @@ the timed cpu_baseline sample), and the oracle's own time on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,6 +55,36 @@ def algorithmic_bytes(shape, fmt: int, pos: int) -> int:
     kv_pos = 2 * L * shape.n_kv_heads * shape.head_dim * 2
     b += kv_pos * (pos + 1) + kv_pos + 4 * V
     return b
+
+
+KERNEL_SOURCES = ("decode_megakernel_cooperative_amd/csrc/amk_decode.hip",
+                  "decode_megakernel_cooperative_amd/csrc/amk_kparams.h",
+                  "decode_megakernel_cooperative_amd/csrc/amk_host.cpp")
+
+
+def kernel_source_hash(root: str = ROOT) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload: str, root: str = ROOT, profiles: str = None):
+    """HBM bytes per decode launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs (each
+    scaled by the same counter's reading on a copy of known size), from the committed profile
+    summary; None when there is none for this workload or the kernel sources changed since."""
+    path = os.path.join(profiles or os.path.join(root, "profiles"), f"decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"traffic-record: (\{.*\})", f.read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_sha256") != kernel_source_hash(root):
+        return None
+    return int(rec["bytes_per_launch"])
 
 
 def main() -> int:
@@ -185,7 +217,7 @@ def main() -> int:
         "achieved_GBps": round(achieved, 1),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": counter_traffic(wl.key)},
         "parity": parity,
         "cpu_baseline": cpu,
     }

@@ -21,7 +21,7 @@ AMK_ERR_INVALID_ARG = -1
 AMK_ERR_UNSUPPORTED = -2
 AMK_ERR_HIP = -3
 AMK_ERR_COOPERATIVE = -4
-AMK_ERR_BARRIER_TIMEOUT = -5
+AMK_ERR_SYNC_TIMEOUT = -5
 AMK_ERR_OOM = -6
 AMK_BF16 = 0
 AMK_W8A16 = 1

@@ -4,19 +4,25 @@
 //
 // Method: the decode-megakernel pages (AutoMegaKernel paper index, Abstract; gist.science
 // explainer, Technical Summary > Problem Statement and Methodology) fuse the forward pass of a
-// Llama-family model into one persistent cooperative kernel whose blocks synchronise through
-// monotonic counters instead of kernel boundaries, and prefetch weights while computing. This
-// file is an MI355X design of that idea, not a translation of the pages' CUDA:
+// Llama-family model into one persistent cooperative kernel whose blocks synchronise inside the
+// launch instead of at kernel boundaries, and prefetch weights while they wait. This file is an
+// MI355X design of that idea, not a translation of the pages' CUDA:
 //
 //  * Grid: one 512-thread block per compute unit (256 on MI355X), launched cooperatively so
 //    all blocks are co-resident. Each GEMV stage splits its row pairs evenly over all 2048
 //    waves; every weight byte is streamed once with coalesced non-temporal dwordx4 loads.
-//  * Barrier: blocks arrive on 8 monotonic counters (block id mod 8, one 128-byte line each)
-//    and lanes 0..7 of wave 0 poll all 8. Counters are never reset: the target of the n-th
-//    barrier is n * (blocks per counter), with a wrap-safe compare. There are no agent-scope
-//    fences: every value that crosses blocks is written and read with agent-coherent (sc1)
-//    accesses, and a block waits for its own stores (s_waitcnt 0) before arriving. Waits are
-//    bounded; a timeout raises a device error flag and every block leaves the kernel.
+//  * Grid-level synchronisation by tagged hand-offs, not barriers: every value one stage passes
+//    to the next (residual, q, K/V of the new position, attention split partials, attention
+//    output, SwiGLU output) is written as a word that carries the producing step's tag beside
+//    the payload (64-bit words: payload low, tag high; SwiGLU: bf16 high, 16 tag bits low). A
+//    consumer block polls exactly the words it needs with agent-coherent (sc1) loads until all
+//    carry the expected tag, so it waits for its own producers only and the data arrives with
+//    the flag in one round trip. Tags grow by 6 per layer plus 1 per launch (the host advances
+//    the base), so words never need clearing. Waits are bounded; a timeout raises a device error
+//    flag and every block leaves the kernel.
+//  * Prefetch across a hand-off: before a block starts polling a stage's input vector it issues
+//    that stage's operand window (row scales, RoPE tables or residual) and its first two weight
+//    items into registers; attention issues its K/V loads before q arrives.
 //  * Activations: the GEMV input vector of a stage (RMSNorm output, attention output, SwiGLU
 //    output) is staged in LDS as fp32 holding bf16-rounded values, in a swizzled layout so the
 //    four 16-byte LDS reads of a lane per weight chunk are bank-conflict free.
@@ -28,8 +34,9 @@
 //  * Attention: split-KV over (kv head, position range) units, one unit per block. The G query
 //    heads of a kv head share every K/V load. Each 16-lane row (hd 128) or 8-lane row (hd 64)
 //    scores one position per step with DPP row reductions and keeps an online softmax; rows
-//    and waves merge in registers and LDS; the last block to finish a kv head (per-head
-//    counter) merges the S split partials by log-sum-exp and writes bf16 attention outputs.
+//    and waves merge in registers and LDS into one tagged partial (values, max, sum) per unit;
+//    then every block of the kv head merges one slice of the head's outputs over all splits by
+//    log-sum-exp weights (DPP segmented reductions) and writes it as tagged bf16 pairs.
 //  * No MFMA: batch-1 decode is a matrix-vector product, far below the MFMA ridge point.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,12 +53,6 @@
 #endif
 #ifndef AMK_PREFETCH_ITEMS
 #define AMK_PREFETCH_ITEMS 2  // GEMV items issued before the barrier in front of a stage (1 or 2)
-#endif
-#ifndef AMK_EARLY_KV
-#define AMK_EARLY_KV 0    // 1: issue the attention K/V prefetch before the QKV GEMV instead of after it
-#endif
-#ifndef AMK_EARLY_WO
-#define AMK_EARLY_WO 0    // 1: issue the O-projection prefetch at the start of attention
 #endif
 
 namespace amk {
@@ -213,7 +214,8 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// grid barrier
+// grid barrier (the library's barrier microbenchmark only: the decode kernel synchronises by
+// tagged hand-offs, whose cost this measures a lower bound against)
 // ------------------------------------------------------------------------------------------
 struct GridBarrier {
   unsigned* ctr;
@@ -320,6 +322,11 @@ __device__ __forceinline__ uint32_t tag_of(const KParams& p, int layer, int whic
   return p.tag0 + static_cast<uint32_t>(layer * kTagsPerLayer + which);
 }
 // byte offset of a tagged buffer inside the tagged region
+// stage-internal stamps (AMK_FINE_TRACE builds only): slot k of layer l after the stage stamps
+__device__ __forceinline__ void fstamp(const KParams& p, int l, int k) {
+  if (AMK_FINE_TRACE && p.trace != nullptr && threadIdx.x == 0)
+    p.trace[static_cast<size_t>(blockIdx.x) * p.trace_stride + 3 + 11 * p.L + l * 16 + k] = wall_clock64();
+}
 __device__ __forceinline__ int toff(const KParams& p, const uint64_t* buf) {
   return static_cast<int>(reinterpret_cast<const uint8_t*>(buf) - reinterpret_cast<const uint8_t*>(p.tagged));
 }
@@ -542,8 +549,8 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 constexpr int kCG = AMK_KCG;  // chunk slots per item: 2 rows x kCG x 16 B dwordx4 loads per lane
 constexpr int kSeg = 32; // pairs per operand window (lane j holds the operand of packed row 2*base + j)
 
-// Registers that carry a GEMV stage's operand window and first two items across the grid
-// barrier in front of the stage.
+// Registers that carry a GEMV stage's operand window and first two items across the wait for
+// the stage's input vector.
 struct GemvRegs {
   i32x4 a0[kCG], a1[kCG], b0[kCG], b1[kCG];
   float wA, wB;
@@ -738,8 +745,8 @@ __device__ __forceinline__ void gemv_segment_start(const KParams& p, __amdgpu_bu
   if (two) gemv_issue(rs, g, base, np, c, R.b0, R.b1);
 }
 
-// Issues the stage's operand window and first two items; called between the arrival at the
-// barrier in front of the stage and the wait, so HBM keeps streaming while the grid syncs.
+// Issues the stage's operand window and first two items; called before the block polls the
+// stage's input vector, so HBM keeps streaming while the producers of that vector finish.
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
@@ -772,10 +779,14 @@ __device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __rest
       gemv_issue(rs, g, base, np, ci, R.b0, R.b1);  // second item was not prefetched
     }
     float acc0 = 0.f, acc1 = 0.f;
+    if (EPI == EPI_QKV) fstamp(p, layer, 12);
     for (int it = 0; it < items; it += 2) {
       gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
+      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 13);
       gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
+      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 14);
       gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
+      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 15);
       gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
     }
   }
@@ -814,7 +825,7 @@ __device__ __forceinline__ AttnUnit attn_unit(const KParams& p) {
 
 // K/V loads of one pipeline step of a wave: U groups of PPW positions, one position per row
 // of LPP lanes. With skip_pos, the current position (written by this step's QKV stage,
-// possibly still in flight) is left out: the prefetch in front of the barrier uses that.
+// possibly still in flight) is left out: the prefetch issued before q arrives uses that.
 template <int HD, int U>
 __device__ __forceinline__ void attn_load(const KParams& p, const AttnUnit& a, __amdgpu_buffer_rsrc_t kr_rs,
                                           __amdgpu_buffer_rsrc_t vr_rs, int gbase, bool skip_pos, i32x4 (&kr)[U],
@@ -898,6 +909,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       attn_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
     };
 
+    fstamp(p, layer, 0);
     float qv[GMAX][8];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
@@ -975,6 +987,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     for (int gb = wave; gb < ngroups; gb += 2 * step) {
       patch_pos(gb, KA, VA);
       compute(gb, KA, VA);
+      if (gb == wave) fstamp(p, layer, 1);
       load(gb + 2 * step, KA, VA);
       if (gb + step < ngroups) {  // uniform
         patch_pos(gb + step, KB, VB);
@@ -999,6 +1012,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         mr[h] = M;
       }
     };
+    fstamp(p, layer, 2);
     if (LPP == 8) merge_rows(std::integral_constant<int, 8>{});
     merge_rows(std::integral_constant<int, 16>{});
     merge_rows(std::integral_constant<int, 32>{});
@@ -1017,6 +1031,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     }
   }
   wg_barrier();
+  fstamp(p, layer, 3);
   if (!a.active) return;
 
   // merge the waves of the block -> this unit's partial (values, max, sum) as tagged words
@@ -1082,6 +1097,7 @@ __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int laye
           av[bq >> 1][1] = __uint_as_float(x1);
         }
       });
+  fstamp(p, layer, 4);
   const uint32_t to_tag = tag_of(p, layer, kTagO);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -1187,10 +1203,11 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
       if (!handoff_done()) return;
     }
     // QKV GEMV -> RoPE; q, K/V(pos) as tagged words, K/V(pos) also into the cache
-    if (AMK_EARLY_KV) attention_prefetch<HD, GMAX>(p, l, AR);
     gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
                            tag_of(p, l, kTagQKV));
-    if (!AMK_EARLY_KV) attention_prefetch<HD, GMAX>(p, l, AR);
+    fstamp(p, l, 5);
+    attention_prefetch<HD, GMAX>(p, l, AR);
+    fstamp(p, l, 6);
     wg_barrier();  // every wave is done with xs
     stamp();
     ok = poll_q_kv<HD>(p, l, qs);
@@ -1211,7 +1228,9 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     // O-projection + residual
     gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, xs, l, l == 0, R,
                              tag_of(p, l, kTagXO));
+    fstamp(p, l, 7);
     gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, false, R);
+    fstamp(p, l, 8);
     wg_barrier();
     stamp();
     ok = norm_from_x<FMT>(p, p.norm_post + static_cast<size_t>(l) * H, tag_of(p, l, kTagXO), xs, red);
@@ -1221,7 +1240,9 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     // gate/up GEMV -> SwiGLU
     gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, xs, l, false, R,
                               tag_of(p, l, kTagM));
+    fstamp(p, l, 9);
     gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
+    fstamp(p, l, 10);
     wg_barrier();
     stamp();
     ok = vector_from_words16<FMT>(p, reinterpret_cast<const uint32_t*>(p.tm), p.F, tag_of(p, l, kTagM), xs);
@@ -1231,6 +1252,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     // down GEMV + residual
     gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, xs, l, false, R,
                              tag_of(p, l, kTagXD));
+    fstamp(p, l, 11);
     if (l + 1 < L)
       gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);

@@ -166,7 +166,7 @@ const char* amk_status_string(int status) {
     case AMK_ERR_UNSUPPORTED: base = "unsupported model or format"; break;
     case AMK_ERR_HIP: base = "HIP runtime error"; break;
     case AMK_ERR_COOPERATIVE: base = "persistent grid cannot be co-resident"; break;
-    case AMK_ERR_BARRIER_TIMEOUT: base = "grid barrier wait timed out on the device"; break;
+    case AMK_ERR_SYNC_TIMEOUT: base = "a grid-level wait (hand-off poll or barrier) timed out on the device"; break;
     case AMK_ERR_OOM: base = "out of memory"; break;
   }
   s = base;
@@ -496,7 +496,7 @@ int amk_sync(amk_model* m, void* stream) {
     HIP_TRY(hipMemset(m->kp.epoch, 0, 4));
     HIP_TRY(hipMemset(m->kp.err, 0, 4));
     HIP_TRY(hipDeviceSynchronize());
-    return fail(AMK_ERR_BARRIER_TIMEOUT, "a decode step abandoned a grid barrier wait");
+    return fail(AMK_ERR_SYNC_TIMEOUT, "a decode step abandoned a hand-off wait");
   }
   return AMK_OK;
 }
@@ -512,7 +512,7 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   info->grid_blocks = m->grid;
   info->block_threads = amk::kThreads;
   info->lds_bytes = m->lds_bytes;
-  // grid-wide hand-offs per step: barriers (barrier kernel) or tagged vector exchanges
+  // grid-wide tagged vector exchanges per step
   // (streaming kernel: RMSNorm input, q, split partials, attention output, RMSNorm input, SwiGLU
   // output per layer, then the final RMSNorm input)
   info->handoffs_per_step = amk::kTagsPerLayer * m->cfg.n_layers + 1;
@@ -598,7 +598,7 @@ int amk_bench_barrier(int32_t iters, float* us_out) {
     unsigned herr = 0;
     if (e == hipSuccess) e = hipMemcpy(&herr, err, 4, hipMemcpyDeviceToHost);
     if (e != hipSuccess) { rc = fail(AMK_ERR_HIP, std::string("barrier bench: ") + hipGetErrorString(e)); break; }
-    if (herr) { rc = fail(AMK_ERR_BARRIER_TIMEOUT, "barrier bench timed out"); break; }
+    if (herr) { rc = fail(AMK_ERR_SYNC_TIMEOUT, "barrier bench timed out"); break; }
     *us_out = ms * 1000.f / static_cast<float>(iters);
   } while (false);
   if (a) hipEventDestroy(a);

@@ -1,47 +1,46 @@
 """Summaries of the per-block stage trace written by the decode kernel (amk_set_trace).
 
-Each block records the 100 MHz wall clock at kernel entry, at the arrival at and exit from every
-grid barrier, and at the end. Per stage s (the work between barrier s-1 and barrier s) this gives
-  busy   = arrival_s - exit_{s-1}       (per block)
-  wait   = exit_s - arrival_s           (per block)
-  skew   = last arrival_s - first arrival_s
-  latency= first exit_s - last arrival_s (propagation of the last arrival to the first waiter)
+Each block records the 100 MHz wall clock at kernel entry (event 0), then 11 events per layer
+(event 1 + 11 l + k, k indexing STAGES: the end of that stage in this block), then the final
+RMSNorm (1 + 11 L) and the end of the lm_head (2 + 11 L). A stage's per-block duration is its
+event minus the block's previous event. Stages whose name ends in "wait" (and the two RMSNorm
+stages, which poll the residual first) are mostly the block waiting for its producers; the others
+are the block's own work plus the prefetch of the next stage.
 """
 from __future__ import annotations
 
 import numpy as np
 
 TICK_US = 0.01  # 100 MHz wall clock
-STAGES = ("qkv", "attn", "o_proj", "gate_up", "down")
+STAGES = ("norm", "qkv", "q_wait", "attn", "merge", "o_wait", "o_proj", "norm2", "gate_up", "m_wait", "down")
 
 
 def events_per_block(n_layers: int) -> int:
-    return 2 + 2 * 5 * n_layers
+    return 3 + len(STAGES) * n_layers
 
 
-def summarize(trace: np.ndarray, n_layers: int) -> dict:
-    """trace: uint64 [grid][events_per_block] from one step. Returns per-stage-kind mean times in us."""
-    t = trace.astype(np.int64)
-    nb = 5 * n_layers
-    t0 = t[:, 0]
-    arr = t[:, 1:1 + 2 * nb:2]
-    ext = t[:, 2:2 + 2 * nb:2]
-    end = t[:, 1 + 2 * nb]
-    prev_exit = np.concatenate([t0[:, None], ext[:, :-1]], axis=1)
-    busy = (arr - prev_exit) * TICK_US
-    wait = (ext - arr) * TICK_US
-    skew = (arr.max(0) - arr.min(0)) * TICK_US
-    lat = (ext.min(0) - arr.max(0)) * TICK_US
-    out = {"total_us": float((end.max() - t0.min()) * TICK_US),
-           "final_stage_us": float((end.max() - ext[:, -1].min()) * TICK_US)}
+def stage_durations(trace: np.ndarray, n_layers: int) -> np.ndarray:
+    """trace: [grid][>= events_per_block] stamps of one step -> [grid][n_layers][11] durations in us."""
+    t = np.asarray(trace, dtype=np.int64)
+    ns = len(STAGES)
+    ev = t[:, 1:1 + ns * n_layers].reshape(t.shape[0], n_layers, ns)
+    prev = np.concatenate([t[:, 0:1], ev[:, :-1, -1]], axis=1)
+    starts = np.concatenate([prev[:, :, None], ev[:, :, :-1]], axis=2)
+    return (ev - starts) * TICK_US
+
+
+def summarize(trace: np.ndarray, n_layers: int, skip_first_layer: bool = True) -> dict:
+    """Mean over layers of each stage's block-mean and block-max duration (us), plus totals."""
+    t = np.asarray(trace, dtype=np.int64)
+    d = stage_durations(t, n_layers)
+    if skip_first_layer and n_layers > 1:
+        d = d[:, 1:]
+    e_end = 2 + len(STAGES) * n_layers
+    out = {
+        "total_us": float((t[:, e_end].max() - t[:, 0].min()) * TICK_US),
+        "lm_head_us": float(((t[:, e_end] - t[:, e_end - 1]) * TICK_US).mean()),
+        "layer_us": float(d.mean(axis=0).sum(axis=-1).mean()),
+    }
     for k, name in enumerate(STAGES):
-        idx = np.arange(k, nb, 5)
-        out[name] = {
-            "busy_max_us": float(busy[:, idx].max(0).mean()),
-            "busy_mean_us": float(busy[:, idx].mean()),
-            "wait_mean_us": float(wait[:, idx].mean()),
-            "skew_us": float(skew[idx].mean()),
-            "latency_us": float(lat[idx].mean()),
-            "span_us": float(((ext.max(0) - np.concatenate([[t0.min()], ext.max(0)[:-1]]))[idx]).mean() * TICK_US),
-        }
+        out[name] = {"mean_us": float(d[:, :, k].mean()), "max_over_blocks_us": float(d[:, :, k].max(axis=0).mean())}
     return out

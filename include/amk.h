@@ -3,8 +3,10 @@
  *
  * One call of amk_decode_step runs the whole forward pass of one decoded token as ONE
  * persistent cooperative kernel launch: RMSNorm, QKV GEMV, RoPE, GQA attention over the
- * KV cache, O-projection, SwiGLU gate/up/down GEMVs and the lm_head GEMV, with grid-wide
- * barriers between dependent stages. This follows the problem statement of the
+ * KV cache, O-projection, SwiGLU gate/up/down GEMVs and the lm_head GEMV, with grid-level
+ * synchronisation between dependent stages done by tagged hand-offs: a stage writes its output
+ * as words that carry the step's tag, and each consumer block polls the words it needs until
+ * they carry that tag (no grid barrier, no counter reset). This follows the problem statement of the
  * decode-megakernel pages: batch-1 decode is bandwidth bound, its latency floor is weight
  * bytes over HBM bandwidth, and per-operator launches plus activation round trips through
  * HBM keep frameworks off that floor (gist.science explainer of AutoMegaKernel, Technical
@@ -35,7 +37,7 @@ extern "C" {
 #define AMK_ERR_UNSUPPORTED (-2)     /* model shape or format outside the supported set    */
 #define AMK_ERR_HIP (-3)             /* a HIP runtime call failed (text via status string) */
 #define AMK_ERR_COOPERATIVE (-4)     /* the persistent grid cannot be co-resident          */
-#define AMK_ERR_BARRIER_TIMEOUT (-5) /* a grid barrier wait exceeded its bound (device)    */
+#define AMK_ERR_SYNC_TIMEOUT (-5)    /* a grid-level wait exceeded its bound (device)      */
 #define AMK_ERR_OOM (-6)             /* host or device allocation failed                   */
 
 #define AMK_BF16 0  /* weights stored bf16, fp32 accumulation                              */
@@ -115,14 +117,14 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_ten
  *   caller-owned; slots [0, pos) must already hold this sequence's keys/values.
  * logits_out: device fp32 [V], caller-owned.
  * Errors (checked on the host before any HIP call): INVALID_ARG for null handle/pointers,
- * token outside [0, V) or pos outside [0, max_ctx); HIP if the launch fails. A barrier
- * timeout of an earlier step is reported as BARRIER_TIMEOUT by amk_sync.
+ * token outside [0, V) or pos outside [0, max_ctx); HIP if the launch fails. A hand-off
+ * timeout of an earlier step is reported as SYNC_TIMEOUT by amk_sync.
  * Concurrency: one handle must not run two steps at once (they share the scratch). */
 int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
                     float* logits_out, void* stream);
 
 /* Waits for `stream` and reports a device-side error raised by earlier steps of this model
- * (AMK_ERR_BARRIER_TIMEOUT), then clears it so the model is usable again. */
+ * (AMK_ERR_SYNC_TIMEOUT), then clears it so the model is usable again. */
 int amk_sync(amk_model* m, void* stream);
 
 /* Bytes of the caller-owned KV cache: L * 2 * nkv * max_ctx * head_dim * 2. 0 for NULL. */
@@ -150,23 +152,23 @@ int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes
 int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
                       float* scales);
 
-/* Measures the library's grid barrier: runs `iters` barriers in one persistent launch on
- * the current device and stores the mean microseconds per barrier in *us_out. Synchronous. */
+/* Measures a classic grid barrier (arrival counters + polling, the pattern the tagged hand-offs
+ * replace) for reference: runs `iters` barriers in one persistent launch on the current device
+ * and stores the mean microseconds per barrier in *us_out. Synchronous. */
 int amk_bench_barrier(int32_t iters, float* us_out);
 
-/* Debug control: bound (in 100 MHz wall-clock ticks) on any single grid-barrier wait or
- * hand-off poll; 0 restores the default (one second). A tiny bound makes steps fail cleanly
- * with BARRIER_TIMEOUT, which is how the timeout path is exercised. */
+/* Debug control: bound (in 100 MHz wall-clock ticks) on any single hand-off poll or barrier
+ * wait; 0 restores the default (one second). A tiny bound makes steps fail cleanly with
+ * SYNC_TIMEOUT, which is how the timeout path is exercised. */
 int amk_set_spin_limit(amk_model* m, uint64_t ticks);
 
 /* Debug control: per-block stage timestamps. When trace is non-NULL, every later step of this
- * model writes, for each block b, the 100 MHz wall clock into trace[b * events_per_block + e].
- * Barrier kernel: e = 0 at kernel entry, then the arrival and the exit of every grid barrier in
- * order, then the end of the lm_head stage (at least 2 + 10 * n_layers events). Streaming
- * kernel: e = 0 at entry, e = 1 when the first RMSNorm is in LDS, then per layer 11 events (QKV
- * epilogue, q received, attention partial stored, split merge stored, attention output received,
- * O epilogue, RMSNorm 2 in LDS, gate/up epilogue, SwiGLU output received, down epilogue, next
- * RMSNorm in LDS), then the end of the lm_head epilogue (at least 3 + 11 * n_layers events).
+ * model writes, for each block b, the 100 MHz wall clock into trace[b * events_per_block + e]:
+ * e = 0 at kernel entry; e = 1 + 11 l + k for layer l and k = 0..10: the layer's RMSNorm in
+ * LDS, QKV epilogue, q received, attention partial stored, split merge stored, attention output
+ * received, O epilogue, RMSNorm 2 in LDS, gate/up epilogue, SwiGLU output received, down
+ * epilogue; e = 1 + 11 L when the final RMSNorm is in LDS and e = 2 + 11 L at the end of the
+ * lm_head (events_per_block >= 3 + 11 * n_layers).
  * trace: device uint64 [grid_blocks][events_per_block], caller-owned. NULL switches tracing off.
  * Errors: INVALID_ARG for a null handle or a too small events_per_block. */
 int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block);

@@ -95,3 +95,40 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(A, "_lib", None)
     with pytest.raises(FileNotFoundError):
         A.lib()
+
+
+def test_trace_summary_layout():
+    """The trace summary reads the kernel's event layout: entry, 11 events per layer, final
+    RMSNorm, lm_head end. A synthetic trace with known per-stage durations comes back exact."""
+    from decode_megakernel_cooperative_amd import trace as T
+    L, nb = 3, 4
+    dur_ticks = np.arange(1, 12) * 10  # stage k takes 10 (k + 1) ticks in every block and layer
+    t = np.zeros((nb, T.events_per_block(L)), dtype=np.int64)
+    for b in range(nb):
+        now = 1000 * b
+        t[b, 0] = now
+        for l in range(L):
+            for k in range(11):
+                now += int(dur_ticks[k]) + b  # block b is b ticks slower per stage
+                t[b, 1 + 11 * l + k] = now
+        t[b, 1 + 11 * L] = now + 5
+        t[b, 2 + 11 * L] = now + 5 + 700
+    s = T.summarize(t, L)
+    for k, name in enumerate(T.STAGES):
+        assert s[name]["mean_us"] == pytest.approx((dur_ticks[k] + 1.5) * 0.01)
+        assert s[name]["max_over_blocks_us"] == pytest.approx((dur_ticks[k] + 3) * 0.01)
+    assert s["lm_head_us"] == pytest.approx(7.0)
+    assert s["layer_us"] == pytest.approx(sum(dur_ticks + 1.5) * 0.01)
+
+
+def test_bench_traffic_record_tracks_kernel_sources(tmp_path):
+    """bench.py reports counter-measured HBM traffic only while the kernel sources are the ones the
+    counters were taken on."""
+    import bench
+    rec = {"workload": "w", "bytes_per_launch": 123456, "kernel_sha256": bench.kernel_source_hash()}
+    (tmp_path / "decode_w_hbm_traffic.md").write_text("notes\ntraffic-record: " + json.dumps(rec) + "\n")
+    assert bench.counter_traffic("w", profiles=str(tmp_path)) == 123456
+    rec["kernel_sha256"] = "0" * 64
+    (tmp_path / "decode_w_hbm_traffic.md").write_text("traffic-record: " + json.dumps(rec) + "\n")
+    assert bench.counter_traffic("w", profiles=str(tmp_path)) is None
+    assert bench.counter_traffic("missing", profiles=str(tmp_path)) is None
