@@ -291,14 +291,9 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   // ---------------- scratch ----------------
   size_t so = 0;
   auto stake = [&](size_t bytes) { size_t o = so; so = align_up(so + bytes, 256); return o; };
-  const size_t s_x = stake(4 * H), s_q = stake(4 * QD), s_o = stake(4 * QD), s_m = stake(4 * F);
-  const size_t s_pacc = stake(4 * static_cast<size_t>(c.n_q_heads) * m->s_cap * hd);
-  const size_t s_pml = stake(4 * static_cast<size_t>(c.n_q_heads) * m->s_cap * 2);
-  const size_t s_gctr = stake(4 * amk::kCtrStride * static_cast<size_t>(c.n_kv_heads));
-  const size_t s_bctr = stake(4 * amk::kCtrStride * amk::kBarrierCtrs);
-  const size_t s_epoch = stake(4 * amk::kCtrStride);
   const size_t s_err = stake(4 * amk::kCtrStride);
-  // tagged exchange words of the streaming kernel (8 bytes each), one contiguous region
+  // tagged exchange words (8 bytes each; the SwiGLU output uses 4-byte words), one contiguous
+  // region so a single buffer resource covers every poll
   const size_t s_tag = so;
   const size_t t_x = stake(8 * H), t_q = stake(8 * QD), t_kv = stake(8 * KD), t_o = stake(8 * QD / 2),
                t_m = stake(8 * F / 2);
@@ -434,16 +429,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   k.rope_cos = reinterpret_cast<const float*>(W + off_cos);
   k.rope_sin = reinterpret_cast<const float*>(W + off_sin);
   uint8_t* S = m->scratch;
-  k.x = reinterpret_cast<float*>(S + s_x);
-  k.q = reinterpret_cast<float*>(S + s_q);
-  k.o = reinterpret_cast<float*>(S + s_o);
-  k.m = reinterpret_cast<float*>(S + s_m);
-  k.pacc = reinterpret_cast<float*>(S + s_pacc);
-  k.pml = reinterpret_cast<float*>(S + s_pml);
   k.s_cap = m->s_cap;
-  k.gctr = reinterpret_cast<unsigned*>(S + s_gctr);
-  k.bctr = reinterpret_cast<unsigned*>(S + s_bctr);
-  k.epoch = reinterpret_cast<unsigned*>(S + s_epoch);
   k.err = reinterpret_cast<unsigned*>(S + s_err);
   k.spin_limit = m->spin_limit;
   k.tagged = reinterpret_cast<uint64_t*>(S + s_tag);
@@ -490,10 +476,8 @@ int amk_sync(amk_model* m, void* stream) {
   unsigned err = 0;
   HIP_TRY(hipMemcpy(&err, m->kp.err, 4, hipMemcpyDeviceToHost));
   if (err != 0) {
-    // counters no longer match the launch history: start over from zero
-    HIP_TRY(hipMemset(m->kp.bctr, 0, 4 * amk::kCtrStride * amk::kBarrierCtrs));
-    HIP_TRY(hipMemset(m->kp.gctr, 0, 4 * amk::kCtrStride * static_cast<size_t>(m->cfg.n_kv_heads)));
-    HIP_TRY(hipMemset(m->kp.epoch, 0, 4));
+    // words the abandoned step left carry older tags than any later step polls for: only the
+    // flag needs clearing
     HIP_TRY(hipMemset(m->kp.err, 0, 4));
     HIP_TRY(hipDeviceSynchronize());
     return fail(AMK_ERR_SYNC_TIMEOUT, "a decode step abandoned a hand-off wait");

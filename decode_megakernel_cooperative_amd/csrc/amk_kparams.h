@@ -7,10 +7,9 @@ namespace amk {
 constexpr int kThreads = 512;          // threads per persistent block (8 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line per counter
-constexpr int kBarrierCtrs = 8;        // arrival counters (block id mod 8)
-constexpr int kStagesPerLayer = 5;     // grid barriers per layer
+constexpr int kBarrierCtrs = 8;        // arrival counters of the barrier microbenchmark
 
-// Tags of the streaming kernel's exchange words: stage `which` of layer l in a launch writes tag
+// Tags of the exchange words: stage `which` of layer l in a launch writes tag
 // tag0 + l * kTagsPerLayer + which; the host advances tag0 by kTagsPerLayer * L + 1 per launch.
 constexpr int kTagsPerLayer = 6;
 enum { kTagQKV = 0, kTagPart = 1, kTagO = 2, kTagXO = 3, kTagM = 4, kTagXD = 5 };
@@ -42,29 +41,21 @@ struct KParams {
   uint16_t* kv;                             // bf16 [L][2][nkv][max_ctx][hd]
   float* logits;                            // fp32 [V]
   // scratch (library-owned)
-  float* x;                                 // residual stream fp32 [H]
-  float* q;                                 // rotated queries fp32 [nq*hd]
-  float* o;                                 // attention output (bf16 values) fp32 [nq*hd]
-  float* m;                                 // SwiGLU output (bf16 values) fp32 [F]
-  float* pacc;                              // split partial sums fp32 [nq][S_cap][hd]
-  float* pml;                               // split max / sum fp32 [nq][S_cap][2]
-  int32_t s_cap;
-  unsigned* gctr;                           // per kv head split counters (stride kCtrStride)
-  unsigned* bctr;                           // barrier arrival counters (stride kCtrStride)
-  unsigned* epoch;                          // barriers completed by earlier launches
+  int32_t s_cap;                            // split capacity per kv head (partials stride)
   unsigned* err;                            // device error flag
-  uint64_t spin_limit;                      // wall-clock ticks per barrier wait / poll
-  // streaming kernel: tagged exchange words (low 32 bits payload, high 32 bits tag), all inside
-  // one region so a single buffer resource covers them
+  uint64_t spin_limit;                      // wall-clock ticks per hand-off poll
+  // tagged exchange words (low 32 bits payload, high 32 bits tag), all inside one region so a
+  // single buffer resource covers them
   uint64_t* tagged; uint32_t tagged_bytes;
   uint64_t* tx;                             // [H] residual (fp32)
   uint64_t* tq;                             // [nq*hd] rotated queries (fp32)
   uint64_t* tkv;                            // [2][nkv][hd/2] K/V of pos, bf16 dims (i, i+hd/2)
   uint64_t* tpart;                          // [nq][s_cap][hd+2] split partials: values, max, sum
   uint64_t* to;                             // [nq*hd/2] attention output, 2 bf16 per word
-  uint64_t* tm;                             // [F/2] SwiGLU output, 2 bf16 per word
+  uint64_t* tm;                             // SwiGLU output: [F] 32-bit words bf16 << 16 | tag & 0xffff
+                                            // (wave-row kernel) or [F/2] 2 bf16 per word (block kernel)
   uint32_t tag0;
-  // streaming kernel: LDS layout (offsets in floats)
+  // block-split kernel: LDS layout (offsets in floats)
   int32_t lds_part, lds_scl, lds_scl_stride, lds_nw, lds_xres, lds_rope;
   uint64_t* trace;                          // optional [grid][trace_stride] wall-clock stamps
   int32_t trace_stride;

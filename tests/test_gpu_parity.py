@@ -96,6 +96,20 @@ def test_long_split_current_position_late_in_unit(fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+def test_block_split_kernel_parity(fmt, monkeypatch):
+    """The alternative block-split kernel (AMK_KERNEL=block at load time) against the oracle on
+    the head_dim-128, 4-queries-per-kv-head case with a multi-split prefilled cache."""
+    monkeypatch.setenv("AMK_KERNEL", "block")
+    shape = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0)
+    dec, orc, kv = build(shape, fmt, 340, 300, seed0=3)
+    assert dec.info().kernel == D.amk.AMK_KERNEL_BLOCK
+    tok = W.gen_tokens(shape, 1, seed0=3)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 300, [], 12, first_token=tok, check_kv=True)
+    _assert_gates(res, f"block kernel fmt{fmt}")
+    dec.close()
+
+
 def test_determinism_and_idempotence():
     """No float atomics: repeated identical steps give bitwise-identical logits and KV entries."""
     wl = W.WORKLOADS["smollm2-135m-w8a16"]
