@@ -95,6 +95,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle steps timed for the cpu baseline")
+    ap.add_argument("--greedy", action="store_true",
+                    help="time device-resident greedy steps: each launch reads the token the previous "
+                         "one wrote (amk_decode_step_greedy), no host involvement between launches")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode kernel runs on a single device "
@@ -140,11 +143,17 @@ def main() -> int:
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     logits_all = torch.empty((steps, shape.vocab), dtype=torch.float32, device=dev)
+    tok_dev = torch.empty(steps + 1, dtype=torch.int32, device=dev)
+    tok_dev[0] = tokens[0]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
-        dec.step(tokens[i], pos0 + i, logits_out=logits_all[i], stream=stream)
+        if args.greedy:
+            dec.step_greedy(tok_dev[i:i + 1], pos0 + i, next_token_out=tok_dev[i + 1:i + 2],
+                            logits_out=logits_all[i], stream=stream)
+        else:
+            dec.step(tokens[i], pos0 + i, logits_out=logits_all[i], stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
@@ -156,6 +165,8 @@ def main() -> int:
     log(f"[bench] {steps} steps: {ms:.3f} ms (wall {wall_ms:.3f} ms) -> {us_per_token:.1f} us/token, "
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
 
+    if args.greedy:  # the oracle follows the tokens the device chain chose
+        tokens = [int(t) for t in tok_dev.cpu().tolist()]
     # parity gate + cpu baseline: the oracle runs the first cpu_steps timed steps on the host
     cpu = None
     parity = None
@@ -211,7 +222,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.key, "positions": f"{pos0}-{pos0 + steps - 1}", "batch": 1,
                    "weights": "int8 per-row scales" if fmt == W.FMT_W8A16 else "bf16", "kv_cache": "bf16",
-                   "grid": f"{info.grid_blocks}x{info.block_threads}"},
+                   "grid": f"{info.grid_blocks}x{info.block_threads}",
+                   "tokens": "device-resident greedy chain" if args.greedy else "host-fed, seeded"},
         "tokens_per_s": round(1e6 / us_per_token, 1),
         "bytes_per_token": int(bytes_mean),
         "achieved_GBps": round(achieved, 1),

@@ -28,7 +28,7 @@ AMK_W8A16 = 1
 AMK_KERNEL_WAVE = 0
 AMK_KERNEL_BLOCK = 1
 
-EXPORTED = ("amk_load_weights", "amk_decode_step", "amk_sync", "amk_kv_cache_bytes", "amk_get_info",
+EXPORTED = ("amk_load_weights", "amk_decode_step", "amk_decode_step_greedy", "amk_sync", "amk_kv_cache_bytes", "amk_get_info",
             "amk_export_quantized", "amk_quantize_int8", "amk_bench_barrier", "amk_set_spin_limit",
             "amk_set_trace", "amk_free", "amk_status_string")
 
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.amk_load_weights.argtypes = [ctypes.POINTER(amk_config), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]
         L.amk_decode_step.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.amk_decode_step_greedy.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.amk_sync.argtypes = [vp, vp]
         L.amk_kv_cache_bytes.argtypes = [vp]
         L.amk_kv_cache_bytes.restype = ctypes.c_size_t
@@ -132,6 +133,18 @@ def amk_decode_step(model: int, token: int, pos: int, kv_cache, logits_out, stre
     kv = kv_cache.data_ptr() if hasattr(kv_cache, "data_ptr") else int(kv_cache or 0)
     lg = logits_out.data_ptr() if hasattr(logits_out, "data_ptr") else int(logits_out or 0)
     _check(lib().amk_decode_step(model, int(token), int(pos), kv, lg, _stream_handle(stream)))
+
+
+def _ptr(x) -> int:
+    return x.data_ptr() if hasattr(x, "data_ptr") else int(x or 0)
+
+
+def amk_decode_step_greedy(model: int, token_in, pos: int, kv_cache, logits_out, next_token_out,
+                           stream=None) -> None:
+    """token_in / next_token_out: device int32 tensors of one element (may be the same tensor);
+    logits_out: device fp32 [V] or None."""
+    _check(lib().amk_decode_step_greedy(model, _ptr(token_in), int(pos), _ptr(kv_cache), _ptr(logits_out),
+                                        _ptr(next_token_out), _stream_handle(stream)))
 
 
 def amk_sync(model: int, stream=None) -> None:
@@ -208,6 +221,14 @@ class Decoder:
         out = self.logits if logits_out is None else logits_out
         amk_decode_step(self.model, token, pos, self.kv, out, stream)
         return out
+
+    def step_greedy(self, token_in, pos: int, next_token_out=None, logits_out=None, stream=None):
+        """Device-resident greedy step: reads the input token from the int32 device tensor
+        token_in, writes the argmax token into next_token_out (default: token_in, in place) and,
+        if logits_out is given, the logits."""
+        nxt = token_in if next_token_out is None else next_token_out
+        amk_decode_step_greedy(self.model, token_in, pos, self.kv, logits_out, nxt, stream)
+        return nxt
 
     def sync(self, stream=None):
         amk_sync(self.model, stream)

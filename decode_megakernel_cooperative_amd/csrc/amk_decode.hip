@@ -259,7 +259,7 @@ struct GridBarrier {
         __builtin_amdgcn_s_sleep(1);
         if (((++it) & 31u) == 0) {
           if (ldc(err) != 0u) { bad = true; break; }
-          if (wall_clock64() - t0 > limit) { stc(err, 1u); bad = true; break; }
+          if (wall_clock64() - t0 > limit) { stc(err, kErrTimeout); bad = true; break; }
         }
       }
       if (bad) *abort_lds = 1;
@@ -322,6 +322,15 @@ __device__ __forceinline__ uint32_t tag_of(const KParams& p, int layer, int whic
   return p.tag0 + static_cast<uint32_t>(layer * kTagsPerLayer + which);
 }
 // byte offset of a tagged buffer inside the tagged region
+// The step's input token: the launch argument, or the device-resident token of a greedy step
+// (read again wherever needed; it does not change during the launch). Out-of-range device tokens
+// decode token 0; the launch reports them through the error flag (see the kernel entry).
+__device__ __forceinline__ int step_token(const KParams& p) {
+  if (p.token_dev == nullptr) return p.token;
+  const int t = __builtin_amdgcn_readfirstlane(*p.token_dev);
+  return (t >= 0 && t < p.V) ? t : 0;
+}
+
 // stage-internal stamps (AMK_FINE_TRACE builds only): slot k of layer l after the stage stamps
 __device__ __forceinline__ void fstamp(const KParams& p, int l, int k) {
   if (AMK_FINE_TRACE && p.trace != nullptr && threadIdx.x == 0)
@@ -367,8 +376,9 @@ __device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_
       unsigned it = 0;
       while (pend != 0u) {
         if (((++it) & 15u) == 0) {
-          if (ldc(p.err) != 0u || wall_clock64() - t_start > p.spin_limit) {
-            stc(p.err, 1u);
+          if (ldc(p.err) != 0u) return false;  // raised elsewhere: keep its code
+          if (wall_clock64() - t_start > p.spin_limit) {
+            stc(p.err, kErrTimeout);
             return false;
           }
         }
@@ -426,8 +436,9 @@ __device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint
       unsigned it = 0;
       while (pend != 0u) {
         if (((++it) & 15u) == 0) {
-          if (ldc(p.err) != 0u || wall_clock64() - t_start > p.spin_limit) {
-            stc(p.err, 1u);
+          if (ldc(p.err) != 0u) return false;  // raised elsewhere: keep its code
+          if (wall_clock64() - t_start > p.spin_limit) {
+            stc(p.err, kErrTimeout);
             return false;
           }
         }
@@ -460,7 +471,7 @@ __device__ __forceinline__ void rmsnorm_embed_to_lds(const KParams& p, const flo
                                                      float* red) {
 #pragma clang fp contract(off)
   const int H = p.H, tid = opaque(threadIdx.x);
-  const uint16_t* row = p.embed + static_cast<size_t>(p.token) * H;
+  const uint16_t* row = p.embed + static_cast<size_t>(step_token(p)) * H;
   float2 xv[kNormVB], wv[kNormVB];
 #pragma unroll
   for (int b = 0; b < kNormVB; ++b) {
@@ -636,7 +647,8 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   if (row < 2 * pb) {
     if (FMT == 1) A = Sc[row];
     if (EPI == EPI_RESID) {
-      B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(p.token) * p.H + row]) : ld_payload(p.tx + row);
+      B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
+                           : ld_payload(p.tx + row);
     } else if (EPI == EPI_QKV) {
       const int half = p.hd >> 1;
       const int i = (row >> 1) % half;
@@ -645,12 +657,20 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   }
 }
 
+// Lane-0 state an epilogue carries across the pairs of one wave: the greedy argmax of the logits
+// seen so far (value, index; rows arrive in increasing order, so a strict compare keeps the
+// lowest index among equal values).
+struct EpiState {
+  float v;
+  int i;
+};
+
 // Runs in lane 0 for one finished row pair: scale (applied by the caller), then q / K / V with
 // RoPE (and the K/V append to the cache), the residual add, SwiGLU, or the logits. Values that
 // cross blocks are written as tagged words (tag tg); a SwiGLU output is one 32-bit word.
 template <int EPI>
 __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1,
-                                         uint32_t tg, float& mprev) {
+                                         uint32_t tg, EpiState& st) {
 #pragma clang fp contract(off)
   if (EPI == EPI_QKV) {
     const int half = p.hd >> 1;
@@ -679,10 +699,19 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
   } else if (EPI == EPI_SWIGLU) {
     const float m = (y0 / (1.0f + expf(-y0))) * y1;
     st_tag16(reinterpret_cast<uint32_t*>(p.tm) + pr, f32_to_bf16(m), tg);
-    (void)mprev;
   } else {
-    p.logits[2 * pr] = y0;
-    p.logits[2 * pr + 1] = y1;
+    if (p.logits != nullptr) {
+      p.logits[2 * pr] = y0;
+      p.logits[2 * pr + 1] = y1;
+    }
+    if (y0 > st.v) {
+      st.v = y0;
+      st.i = 2 * pr;
+    }
+    if (y1 > st.v) {
+      st.v = y1;
+      st.i = 2 * pr + 1;
+    }
   }
 }
 
@@ -710,7 +739,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
                                              const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
                                              float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
-                                             float& mprev) {
+                                             EpiState& st) {
   constexpr int CW = Fmt<FMT>::CW;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
@@ -728,7 +757,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
-      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1, tg, mprev);
+      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1, tg, st);
     }
     c.advance(g.cpp);
   }
@@ -758,13 +787,14 @@ __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* _
 
 // Runs the stage. Items alternate between the two register buffers, each refilled two items
 // ahead of its use; the loop body is branch free apart from the per-pair epilogue, so loads
-// stay in flight across iterations.
+// stay in flight across iterations. Returns the epilogue state of lane 0 (the wave's argmax for
+// the logits stage).
 template <int FMT, int EPI>
-__device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __restrict__ W,
+__device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __restrict__ W,
                                          const float* __restrict__ Sc, int K, int npairs, const float* xs,
                                          int layer, bool rfe, GemvRegs& R, uint32_t tg) {
   const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), 1);
-  float mprev = 0.f;
+  EpiState st{-__builtin_inff(), 0x7fffffff};
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   const float* xlane = xs + __lane_id() * 4;
   for (int base = g.pa; base < g.pb; base += kSeg) {
@@ -781,15 +811,16 @@ __device__ __forceinline__ void gemv_run(const KParams& p, const uint8_t* __rest
     float acc0 = 0.f, acc1 = 0.f;
     if (EPI == EPI_QKV) fstamp(p, layer, 12);
     for (int it = 0; it < items; it += 2) {
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, st);
       if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 13);
       gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
       if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 14);
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, mprev);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, st);
       if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 15);
       gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
     }
   }
+  return st;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1157,15 +1188,81 @@ __device__ __forceinline__ bool poll_q_kv(const KParams& p, int layer, float* qs
       });
 }
 
+// Greedy next token (argmax of the logits, ties to the lowest index) of a device-resident step.
+// Every block reduces its waves' argmax and publishes it as two tagged words (value bits, index);
+// block 0 polls all blocks' words and writes the token. Block 0 therefore writes only after every
+// block has finished the lm_head, so the output may alias the step's input token.
+__device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+__device__ __forceinline__ bool greedy_token(const KParams& p, const EpiState& st, float* smem, float* red,
+                                             int* ired) {
+  const int lane = __lane_id(), wave = wave_id();
+  const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.v), 0));
+  const int wi = __builtin_amdgcn_readlane(st.i, 0);
+  if (lane == 0) {
+    red[wave] = wv;
+    ired[wave] = wi;
+  }
+  wg_barrier();
+  const uint32_t tag = tag_of(p, p.L, 0);
+  if (threadIdx.x == 0) {
+    float bv = red[0];
+    int bi = ired[0];
+    for (int w = 1; w < kWaves; ++w)
+      if (argmax_better(red[w], ired[w], bv, bi)) {
+        bv = red[w];
+        bi = ired[w];
+      }
+    st_tag(p.targ + 2 * blockIdx.x, __float_as_uint(bv), tag);
+    st_tag(p.targ + 2 * blockIdx.x + 1, static_cast<uint32_t>(bi), tag);
+  }
+  if (blockIdx.x != 0) return true;
+  float* av = smem;
+  int* ai = reinterpret_cast<int*>(smem + kThreads);
+  const int ob = toff(p, p.targ);
+  const bool ok = poll_block<1>(p, static_cast<int>(gridDim.x), tag, [&](int qi) { return ob + 16 * qi; },
+                                [&](int, int qi, uint32_t v, uint32_t i) {
+                                  av[qi] = __uint_as_float(v);
+                                  ai[qi] = static_cast<int>(i);
+                                });
+  wg_barrier();
+  if (ok && threadIdx.x < 64) {  // wave 0: a strided pass over the blocks, then a lane tree
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    for (int b = threadIdx.x; b < static_cast<int>(gridDim.x); b += 64)
+      if (argmax_better(av[b], ai[b], bv, bi)) {
+        bv = av[b];
+        bi = ai[b];
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (argmax_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (threadIdx.x == 0) *p.next_token = bi;
+  }
+  return ok;
+}
+
 template <int HD, int FMT, int GMAX>
 __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float red[kWaves];
+  __shared__ int ired[kWaves];
   __shared__ int abort_flag;
   if (threadIdx.x == 0) abort_flag = 0;
   const unsigned err0 = ldc(p.err);
   __syncthreads();
   if (err0 != 0u) return;
+  if (p.token_dev != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    const int t = *p.token_dev;
+    if (t < 0 || t >= p.V) stc(p.err, kErrBadToken);  // the step decodes token 0 and is abandoned
+  }
   uint64_t* trace = p.trace ? p.trace + static_cast<size_t>(blockIdx.x) * p.trace_stride : nullptr;
   int ev = 0;
   auto stamp = [&]() {
@@ -1265,9 +1362,10 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
   stamp();
   if (!handoff_done()) return;
-  gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
+  const EpiState st = gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
   wg_barrier();
   stamp();
+  if (p.next_token != nullptr) greedy_token(p, st, smem, red, ired);
 }
 
 // barrier microbenchmark: `iters` grid barriers in one persistent launch

@@ -298,6 +298,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   const size_t t_x = stake(8 * H), t_q = stake(8 * QD), t_kv = stake(8 * KD), t_o = stake(8 * QD / 2),
                t_m = stake(8 * F / 2);
   const size_t t_part = stake(8 * static_cast<size_t>(c.n_q_heads) * m->s_cap * (hd + 2));
+  const size_t t_arg = stake(16 * static_cast<size_t>(m->grid));
   const size_t s_tag_end = so;
   m->scratch_bytes = so;
 
@@ -440,16 +441,20 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   k.to = reinterpret_cast<uint64_t*>(S + t_o);
   k.tm = reinterpret_cast<uint64_t*>(S + t_m);
   k.tpart = reinterpret_cast<uint64_t*>(S + t_part);
+    k.targ = reinterpret_cast<uint64_t*>(S + t_arg);
   *out = m;
   return AMK_OK;
 }
 
-int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, float* logits_out, void* stream) {
-  if (!m || !kv_cache || !logits_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
-  if (token < 0 || token >= m->cfg.vocab) return fail(AMK_ERR_INVALID_ARG, "token out of range");
-  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
+namespace {
+// One decode step: a single cooperative launch. token_dev / next_token are null for a
+// host-token step.
+int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t pos, void* kv_cache,
+                float* logits_out, int32_t* next_token, void* stream) {
   amk::KParams k = m->kp;
   k.token = token;
+  k.token_dev = token_dev;
+  k.next_token = next_token;
   k.pos = pos;
   const int ctx = pos + 1;
   // split-KV plan: at most s_cap splits per kv head (one attention unit per block), at least
@@ -469,6 +474,22 @@ int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, fl
                                      static_cast<unsigned>(m->lds_bytes), static_cast<hipStream_t>(stream)));
   return AMK_OK;
 }
+}  // namespace
+
+int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, float* logits_out, void* stream) {
+  if (!m || !kv_cache || !logits_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
+  if (token < 0 || token >= m->cfg.vocab) return fail(AMK_ERR_INVALID_ARG, "token out of range");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
+  return launch_step(m, token, nullptr, pos, kv_cache, logits_out, nullptr, stream);
+}
+
+int amk_decode_step_greedy(amk_model* m, const int32_t* token_in, int32_t pos, void* kv_cache, float* logits_out,
+                           int32_t* next_token_out, void* stream) {
+  if (!m || !token_in || !kv_cache || !next_token_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
+  if (m->stream) return fail(AMK_ERR_UNSUPPORTED, "greedy steps run on the wave-row kernel only");
+  return launch_step(m, 0, token_in, pos, kv_cache, logits_out, next_token_out, stream);
+}
 
 int amk_sync(amk_model* m, void* stream) {
   if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
@@ -480,6 +501,8 @@ int amk_sync(amk_model* m, void* stream) {
     // flag needs clearing
     HIP_TRY(hipMemset(m->kp.err, 0, 4));
     HIP_TRY(hipDeviceSynchronize());
+    if (err == amk::kErrBadToken)
+      return fail(AMK_ERR_INVALID_ARG, "a greedy step read a device token outside [0, vocab)");
     return fail(AMK_ERR_SYNC_TIMEOUT, "a decode step abandoned a hand-off wait");
   }
   return AMK_OK;

@@ -12,6 +12,9 @@ constexpr int kBarrierCtrs = 8;        // arrival counters of the barrier microb
 // Tags of the exchange words: stage `which` of layer l in a launch writes tag
 // tag0 + l * kTagsPerLayer + which; the host advances tag0 by kTagsPerLayer * L + 1 per launch.
 constexpr int kTagsPerLayer = 6;
+// device error flag values
+constexpr unsigned kErrTimeout = 1;   // a hand-off poll (or barrier wait) exceeded spin_limit
+constexpr unsigned kErrBadToken = 2;  // a device-resident input token was outside [0, V)
 enum { kTagQKV = 0, kTagPart = 1, kTagO = 2, kTagXO = 3, kTagM = 4, kTagXD = 5 };
 
 struct KParams {
@@ -20,6 +23,8 @@ struct KParams {
   float eps, attn_scale;
   // this step
   int32_t token, pos, S, T;
+  const int32_t* token_dev;                 // greedy step: input token in device memory (else null)
+  int32_t* next_token;                      // greedy step: argmax of the logits (else null)
   // packed weights: per layer, rows are stored in the order the kernel consumes them
   const uint8_t* w_qkv; int64_t w_qkv_ls;   // bytes per layer
   const float* s_qkv;   int64_t s_qkv_ls;   // fp32 scales per layer (W8A16 only)
@@ -52,6 +57,7 @@ struct KParams {
   uint64_t* tkv;                            // [2][nkv][hd/2] K/V of pos, bf16 dims (i, i+hd/2)
   uint64_t* tpart;                          // [nq][s_cap][hd+2] split partials: values, max, sum
   uint64_t* to;                             // [nq*hd/2] attention output, 2 bf16 per word
+  uint64_t* targ;                           // [grid][2] greedy step: each block's argmax (value, index)
   uint64_t* tm;                             // SwiGLU output: [F] 32-bit words bf16 << 16 | tag & 0xffff
                                             // (wave-row kernel) or [F/2] 2 bf16 per word (block kernel)
   uint32_t tag0;

@@ -714,8 +714,9 @@ __device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_
     unsigned it = 0;
     while (pend != 0u) {
       if (((++it) & 15u) == 0) {
-        if (ldc(p.err) != 0u || wall_clock64() - t_start > p.spin_limit) {
-          stc(p.err, 1u);
+        if (ldc(p.err) != 0u) return false;  // raised elsewhere: keep its code
+        if (wall_clock64() - t_start > p.spin_limit) {
+          stc(p.err, kErrTimeout);
           return false;
         }
       }

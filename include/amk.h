@@ -123,8 +123,28 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_ten
 int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
                     float* logits_out, void* stream);
 
+/* Greedy decode step with device-resident tokens (no host round trip per token): the same
+ * forward pass as amk_decode_step, but the input token is read from device memory and the step
+ * also writes the greedy next token: the argmax over the logits, with ties going to the lowest
+ * index. The pages decode greedily (AutoMegaKernel paper index, Abstract); the tie rule is this
+ * library's, and it matches numpy.argmax. Passing one step's next_token_out as the next step's
+ * token_in (with pos + 1) decodes a sequence with no host synchronisation; such a chain of
+ * launches can be captured in a HIP graph.
+ * token_in: device int32 [1], read once the launch starts; next_token_out: device int32 [1],
+ *   written at the end of the step (it may be the same buffer as token_in);
+ * logits_out: device fp32 [V] or NULL (then no logits are written);
+ * kv_cache, pos, stream: as for amk_decode_step. All buffers are caller-owned.
+ * Errors: INVALID_ARG for a null handle, token_in, kv_cache or next_token_out, or pos outside
+ * [0, max_ctx) (host checks, before any HIP call); UNSUPPORTED if the model runs the block-split
+ * kernel; HIP if the launch fails. A token_in value outside [0, V) cannot be checked on the host:
+ * the step then decodes token 0, is abandoned, and amk_sync reports INVALID_ARG. */
+int amk_decode_step_greedy(amk_model* m, const int32_t* token_in, int32_t pos, void* kv_cache,
+                           float* logits_out, int32_t* next_token_out, void* stream);
+
 /* Waits for `stream` and reports a device-side error raised by earlier steps of this model
- * (AMK_ERR_SYNC_TIMEOUT), then clears it so the model is usable again. */
+ * (AMK_ERR_SYNC_TIMEOUT for an abandoned hand-off wait, AMK_ERR_INVALID_ARG for an out-of-range
+ * device token of a greedy step), then clears it so the model is usable again. Steps launched
+ * after the error and before amk_sync do nothing. */
 int amk_sync(amk_model* m, void* stream);
 
 /* Bytes of the caller-owned KV cache: L * 2 * nkv * max_ctx * head_dim * 2. 0 for NULL. */

@@ -77,6 +77,7 @@ def test_argument_validation_without_gpu():
         assert st == A.AMK_ERR_UNSUPPORTED, (field, st, D.amk_status_string(st))
     # calls on a null handle
     assert lib.amk_decode_step(None, 0, 0, None, None, None) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_decode_step_greedy(None, None, 0, None, None, None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_sync(None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_kv_cache_bytes(None) == 0
     assert lib.amk_free(None) == A.AMK_OK
