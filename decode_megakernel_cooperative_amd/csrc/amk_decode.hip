@@ -51,6 +51,14 @@
 #ifndef AMK_KCG
 #define AMK_KCG 2         // 1 KB chunk slots per GEMV item (per row)
 #endif
+#ifndef AMK_STRIDED
+#define AMK_STRIDED 2     // how a GEMV stage's row pairs map to the NW waves of the grid:
+                          // 2: wave w of block b is stream s = w * blocks + b and takes pairs s,
+                          //    s + NW, ...: at any moment the grid streams one sliding window of
+                          //    the matrix, consecutive pairs going to consecutive blocks (and so to
+                          //    different XCDs); 1: the same with s = b * 8 + w; 0: a contiguous
+                          //    range of pairs per wave
+#endif
 #ifndef AMK_PREFETCH_ITEMS
 #define AMK_PREFETCH_ITEMS 2  // GEMV items issued before the barrier in front of a stage (1 or 2)
 #endif
@@ -576,8 +584,10 @@ struct GemvPlan {
   int RB;   // bytes per row
   int nch;  // 1 KB chunks per row
   int cpp;  // padded slots per pair: 1, 2 or 4 when nch <= kCG, else a multiple of kCG
-  int pa, pb;
+  int pa, pb;     // the wave's pairs, as local indices k in [pa, pb)
+  int st0, sst;   // local index k is pair st0 + k * sst of the matrix
 };
+__device__ __forceinline__ int pidx(const GemvPlan& g, int k) { return g.st0 + k * g.sst; }
 
 // Pairs are split over the waves in units of `unit` pairs (2 for gate/up, so a wave's SwiGLU
 // outputs fill whole two-value exchange words).
@@ -588,9 +598,20 @@ __device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave, int u
   g.nch = (g.RB + 1023) >> 10;
   g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
   const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+  if (AMK_STRIDED) {
+    const int sw = AMK_STRIDED == 2 ? wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x) : gw;
+    g.pa = 0;
+    g.pb = sw < npairs ? (npairs - sw + NW - 1) / NW : 0;
+    g.st0 = sw;
+    g.sst = NW;
+    (void)unit;
+    return g;
+  }
   const int nu = npairs / unit;
   g.pa = unit * static_cast<int>((static_cast<int64_t>(nu) * gw) / NW);
   g.pb = unit * static_cast<int>((static_cast<int64_t>(nu) * (gw + 1)) / NW);
+  g.st0 = 0;
+  g.sst = 1;
   return g;
 }
 
@@ -634,17 +655,18 @@ __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const 
   }
 }
 
-// Per-pair operands for a window of 32 pairs: lane j holds the value for packed row
-// 2 * (window base) + j: A = W8A16 row scale, B = residual input (EPI_RESID) or RoPE cos
+// Per-pair operands for a window of 32 pairs: lane j holds the value for row j & 1 of the
+// window's pair j / 2: A = W8A16 row scale, B = residual input (EPI_RESID) or RoPE cos
 // (even j) / sin (odd j) of the pair (EPI_QKV).
 template <int FMT, int EPI>
-__device__ __forceinline__ void load_window(const KParams& p, const float* __restrict__ Sc, int wbase,
-                                            int pb, bool resid_from_embed, float& A, float& B) {
+__device__ __forceinline__ void load_window(const KParams& p, const float* __restrict__ Sc, const GemvPlan& g,
+                                            int wbase, bool resid_from_embed, float& A, float& B) {
   const int lane = __lane_id();
-  const int row = 2 * wbase + lane;
+  const int k = wbase + (lane >> 1);
+  const int row = 2 * pidx(g, k) + (lane & 1);
   A = 1.f;
   B = 0.f;
-  if (row < 2 * pb) {
+  if (k < g.pb) {
     if (FMT == 1) A = Sc[row];
     if (EPI == EPI_RESID) {
       B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
@@ -726,7 +748,7 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const Gemv
     const int off = c.ch * 1024 + lane * 16;
     const int voff = (v && off < g.RB) ? off : kOOB;
     // uniform by construction; readfirstlane keeps the compiler from moving it to VGPRs
-    const int soff = __builtin_amdgcn_readfirstlane(v ? 2 * (base + c.k) * g.RB : 0);
+    const int soff = __builtin_amdgcn_readfirstlane(v ? 2 * pidx(g, base + c.k) * g.RB : 0);
     r0[s] = ldbuf(rs, voff, soff);
     r1[s] = ldbuf(rs, voff, soff + g.RB);
     c.advance(g.cpp);
@@ -757,7 +779,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
-      if (__lane_id() == 0) epilogue<EPI>(p, layer, base + c.k, y0, y1, b0, b1, tg, st);
+      if (__lane_id() == 0) epilogue<EPI>(p, layer, pidx(g, base + c.k), y0, y1, b0, b1, tg, st);
     }
     c.advance(g.cpp);
   }
@@ -768,7 +790,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_segment_start(const KParams& p, __amdgpu_buffer_rsrc_t rs,
                                                    const float* __restrict__ Sc, const GemvPlan& g, int base,
                                                    int np, bool rfe, bool two, GemvRegs& R) {
-  load_window<FMT, EPI>(p, Sc, base, g.pb, rfe, R.wA, R.wB);
+  load_window<FMT, EPI>(p, Sc, g, base, rfe, R.wA, R.wB);
   Cursor c{0, 0};
   gemv_issue(rs, g, base, np, c, R.a0, R.a1);
   if (two) gemv_issue(rs, g, base, np, c, R.b0, R.b1);
