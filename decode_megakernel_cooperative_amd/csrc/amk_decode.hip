@@ -159,7 +159,9 @@ __device__ __forceinline__ float i8_to_f32(int v, int k) {
 // ------------------------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  // every lane of the row patterns used here reads a lane of its own row; written as an update
+  // with a zero fill so the compiler folds the move into the consuming add / max (one DPP op)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 // sum over the 2^k lanes of each aligned group (k = 3: 8 lanes, k = 4: 16 lanes), in every lane
 template <int LANES>
