@@ -45,12 +45,15 @@ def algorithmic_bytes(shape, fmt: int, pos: int) -> int:
     of position pos, and the fp32 logits. Activation scratch (KB per stage) is excluded."""
     H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
     qkv_rows = shape.q_dim + 2 * shape.kv_dim
-    wb = 1 if fmt == W.FMT_W8A16 else 2
-    rows = L * (qkv_rows + H + 2 * F + H) + V
-    mat = L * (qkv_rows * H + H * shape.q_dim + 2 * F * H + H * F) + V * H
-    b = mat * wb
-    if fmt == W.FMT_W8A16:
+    wb = 2 if fmt == W.FMT_BF16 else 1                # projections
+    lmb = 1 if fmt == W.FMT_W8A16 else 2              # lm_head
+    rows = L * (qkv_rows + H + 2 * F + H)
+    mat = L * (qkv_rows * H + H * shape.q_dim + 2 * F * H + H * F)
+    b = mat * wb + V * H * lmb
+    if fmt != W.FMT_BF16:
         b += 4 * rows
+    if fmt == W.FMT_W8A16:
+        b += 4 * V
     b += 2 * H * (2 * L + 1) + 2 * H
     kv_pos = 2 * L * shape.n_kv_heads * shape.head_dim * 2
     b += kv_pos * (pos + 1) + kv_pos + 4 * V
@@ -218,10 +221,11 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "w8a16" if fmt == W.FMT_W8A16 else "bf16",
+        "dtype": wl.fmt_name,
         "data": "synthetic",
         "config": {"workload": wl.key, "positions": f"{pos0}-{pos0 + steps - 1}", "batch": 1,
-                   "weights": "int8 per-row scales" if fmt == W.FMT_W8A16 else "bf16", "kv_cache": "bf16",
+                   "weights": {W.FMT_BF16: "bf16", W.FMT_W8A16: "int8 per-row scales",
+                               W.FMT_W8A16_BF16_HEAD: "int8 per-row scales, bf16 lm_head"}[fmt], "kv_cache": "bf16",
                    "grid": f"{info.grid_blocks}x{info.block_threads}",
                    "tokens": "device-resident greedy chain" if args.greedy else "host-fed, seeded"},
         "tokens_per_s": round(1e6 / us_per_token, 1),

@@ -25,6 +25,7 @@ AMK_ERR_SYNC_TIMEOUT = -5
 AMK_ERR_OOM = -6
 AMK_BF16 = 0
 AMK_W8A16 = 1
+AMK_W8A16_BF16_HEAD = 2
 AMK_KERNEL_WAVE = 0
 AMK_KERNEL_BLOCK = 1
 

@@ -1377,16 +1377,21 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     if (l + 1 < L)
       gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);
+    else if (FMT == 1 && p.lm_fmt == 0)  // int8 projections, bf16 lm_head
+      gemv_prefetch<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
     else
       gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
     wg_barrier();
     stamp();
   }
-  // final RMSNorm -> lm_head
-  ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
+  // final RMSNorm -> lm_head (in the lm_head's own storage format, which sets the LDS layout)
+  const bool head16 = FMT == 1 && p.lm_fmt == 0;
+  if (head16) ok = norm_from_x<0>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
+  else ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
   stamp();
   if (!handoff_done()) return;
-  const EpiState st = gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
+  const EpiState st = head16 ? gemv_run<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u)
+                             : gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
   wg_barrier();
   stamp();
   if (p.next_token != nullptr) greedy_token(p, st, smem, red, ired);

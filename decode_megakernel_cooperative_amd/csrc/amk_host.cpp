@@ -126,7 +126,8 @@ int validate_config(const amk_config* c) {
   if (c->hidden > 8192) return fail(AMK_ERR_UNSUPPORTED, "hidden > 8192");
   if (c->ffn > 32768 || c->n_q_heads * c->head_dim > 32768) return fail(AMK_ERR_UNSUPPORTED, "ffn or q dim > 32768");
   if (c->vocab % 2) return fail(AMK_ERR_UNSUPPORTED, "vocab must be even");
-  if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16) return fail(AMK_ERR_UNSUPPORTED, "weight_format");
+  if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16 && c->weight_format != AMK_W8A16_BF16_HEAD)
+    return fail(AMK_ERR_UNSUPPORTED, "weight_format");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(AMK_ERR_UNSUPPORTED, "rms_eps / rope_theta");
   return AMK_OK;
 }
@@ -196,7 +197,8 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
   const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd;
   const int64_t QKV = QD + 2 * KD;
-  const bool q8 = c.weight_format == AMK_W8A16;
+  const bool q8 = c.weight_format != AMK_BF16;         // int8 projections
+  const bool lm_q8 = c.weight_format == AMK_W8A16;     // int8 lm_head
   const int64_t wb = q8 ? 1 : 2;
 
   auto m = new amk_model();
@@ -220,15 +222,15 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   m->off_o = take(l_o * L);
   m->off_gu = take(l_gu * L);
   m->off_d = take(l_d * L);
-  const bool lm_shares_embed = !q8 && c.tied_embeddings;
-  m->off_lm = lm_shares_embed ? off_embed : take(static_cast<size_t>(V * H * wb));
+  const bool lm_shares_embed = !lm_q8 && c.tied_embeddings;
+  m->off_lm = lm_shares_embed ? off_embed : take(static_cast<size_t>(V * H * (lm_q8 ? 1 : 2)));
   if (q8) {
     m->off_sqkv = take(4 * QKV * L);
     m->off_so = take(4 * H * L);
     m->off_sgu = take(4 * 2 * F * L);
     m->off_sd = take(4 * H * L);
-    m->off_slm = take(4 * V);
   }
+  if (lm_q8) m->off_slm = take(4 * V);
   const size_t off_nin = take(4 * H * L), off_npost = take(4 * H * L), off_nfin = take(4 * H);
   const size_t off_cos = take(4 * static_cast<size_t>(c.max_ctx) * (hd / 2));
   const size_t off_sin = take(4 * static_cast<size_t>(c.max_ctx) * (hd / 2));
@@ -240,7 +242,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   m->gmax = G <= 4 ? 4 : 8;
   {
     const char* kv = std::getenv("AMK_KERNEL");
-    m->stream = kv && std::string(kv) == "block";
+    m->stream = kv && std::string(kv) == "block" && c.weight_format != AMK_W8A16_BF16_HEAD;
   }
   if (m->stream && m->gmax != 4) m->stream = false;  // the block-split kernel covers G <= 4
   // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
@@ -320,10 +322,10 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     return AMK_OK;
   };
   // Packs rows of one layer's matrix given a row map (packed row -> source pointer).
-  auto pack_matrix = [&](int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
+  auto pack_matrix = [&](bool quant, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
                          const std::vector<const uint16_t*>& src_tensors,
                          auto&& row_source) -> int {
-    if (q8) {
+    if (quant) {
       // quantize each source tensor in canonical order, then permute rows
       std::vector<std::vector<int8_t>> qc(src_tensors.size());
       std::vector<std::vector<float>> qs(src_tensors.size());
@@ -362,23 +364,24 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
       nin[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[0][i]);
       npost[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[5][i]);
     }
-    rc = pack_matrix(QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
+    rc = pack_matrix(q8, QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
                      [&](int64_t r, int* w, int64_t* sr) { qkv_source(c, r, w, sr); });
     if (rc) break;
-    rc = pack_matrix(H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
+    rc = pack_matrix(q8, H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
     if (rc) break;
-    rc = pack_matrix(2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
+    rc = pack_matrix(q8, 2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = static_cast<int>(r & 1); *sr = r >> 1; });
     if (rc) break;
-    rc = pack_matrix(H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
+    rc = pack_matrix(q8, H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) {
     for (int64_t i = 0; i < H; ++i) nfin[static_cast<size_t>(i)] = bf16_to_float(t[1 + 9 * L][i]);
     const uint16_t* lm = c.tied_embeddings ? t[0] : t[2 + 9 * L];
     if (!lm_shares_embed)
-      rc = pack_matrix(V, H, m->off_lm, m->off_slm, {lm}, [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
+      rc = pack_matrix(lm_q8, V, H, m->off_lm, m->off_slm, {lm},
+                       [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) rc = upload(off_nin, nin.data(), nin.size() * 4);
   if (rc == AMK_OK) rc = upload(off_npost, npost.data(), npost.size() * 4);
@@ -421,8 +424,9 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     k.s_o = reinterpret_cast<const float*>(W + m->off_so); k.s_o_ls = H;
     k.s_gu = reinterpret_cast<const float*>(W + m->off_sgu); k.s_gu_ls = 2 * F;
     k.s_d = reinterpret_cast<const float*>(W + m->off_sd); k.s_d_ls = H;
-    k.s_lm = reinterpret_cast<const float*>(W + m->off_slm);
   }
+  if (lm_q8) k.s_lm = reinterpret_cast<const float*>(W + m->off_slm);
+  k.lm_fmt = lm_q8 ? 1 : 0;
   k.embed = reinterpret_cast<const uint16_t*>(W + off_embed);
   k.norm_in = reinterpret_cast<const float*>(W + off_nin);
   k.norm_post = reinterpret_cast<const float*>(W + off_npost);
@@ -534,7 +538,7 @@ int amk_get_info(const amk_model* m, amk_info* info) {
 int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, float* scales_out) {
   if (!m || !codes_out || !scales_out) return fail(AMK_ERR_INVALID_ARG, "null pointer");
   const amk_config& c = m->cfg;
-  if (c.weight_format != AMK_W8A16) return fail(AMK_ERR_UNSUPPORTED, "model is not W8A16");
+  if (c.weight_format == AMK_BF16) return fail(AMK_ERR_UNSUPPORTED, "model is not W8A16");
   const int L = c.n_layers;
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
   const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd, QKV = QD + 2 * KD;
@@ -544,6 +548,7 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
   int which = -1;           // which source tensor of a fused matrix we export
   int kind = -1;            // 0 qkv, 1 o, 2 gu, 3 d, 4 lm
   if (idx == lm_idx) {
+    if (c.weight_format != AMK_W8A16) return fail(AMK_ERR_INVALID_ARG, "the lm_head of this model is not quantized");
     kind = 4; rows = mrows = V; cols = H; wsrc = m->off_lm; ssrc = m->off_slm;
   } else if (idx >= 1 && idx < 1 + 9 * L) {
     const int l = (idx - 1) / 9, o = (idx - 1) % 9;

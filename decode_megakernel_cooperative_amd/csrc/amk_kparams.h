@@ -36,6 +36,7 @@ struct KParams {
   const float* s_d;     int64_t s_d_ls;
   const uint8_t* w_lm;
   const float* s_lm;
+  int32_t lm_fmt;                           // lm_head storage: 0 bf16, 1 int8 (+ s_lm)
   const uint16_t* embed;                    // bf16 [V][H]
   const float* norm_in;                     // fp32 [L][H]
   const float* norm_post;                   // fp32 [L][H]

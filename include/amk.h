@@ -42,6 +42,8 @@ extern "C" {
 
 #define AMK_BF16 0  /* weights stored bf16, fp32 accumulation                              */
 #define AMK_W8A16 1 /* weights int8, one fp32 scale per output row; activations bf16      */
+#define AMK_W8A16_BF16_HEAD 2 /* AMK_W8A16 projections, lm_head kept bf16 (for a tied model the
+                                 head reads the bf16 embedding table; no quantized copy)      */
 
 /* Model description. Weights follow HuggingFace LlamaForCausalLM: pre-norm RMSNorm,
  * rotate-half RoPE with inv_freq_i = rope_theta^(-2i/head_dim), grouped-query attention
@@ -60,7 +62,7 @@ typedef struct {
   float rms_eps;           /* RMSNorm epsilon                                                */
   float rope_theta;        /* RoPE base                                                      */
   int32_t tied_embeddings; /* 1: lm_head is embed_tokens                                     */
-  int32_t weight_format;   /* AMK_BF16 or AMK_W8A16                                          */
+  int32_t weight_format;   /* AMK_BF16, AMK_W8A16 or AMK_W8A16_BF16_HEAD                     */
 } amk_config;
 
 typedef struct amk_model amk_model; /* opaque, library-owned */
@@ -90,7 +92,7 @@ typedef struct {
   int32_t kernel;               /* AMK_KERNEL_WAVE or AMK_KERNEL_BLOCK                       */
 } amk_info;
 
-/* Copies, packs, (for AMK_W8A16) quantizes and uploads a model to the current device.
+/* Copies, packs, (for the W8A16 formats) quantizes and uploads a model to the current device.
  * host_bf16_tensors: n_tensors host pointers to bf16 bit patterns (uint16), row-major
  *   [out][in] for matrices, in canonical HF order:
  *     embed_tokens [V][H];
@@ -101,6 +103,10 @@ typedef struct {
  *   n_tensors must equal 2 + 9 L + (tied ? 0 : 1).
  * W8A16 quantizes every projection and the lm_head (for tied models: a quantized copy of
  * embed_tokens; the embedding gather keeps reading bf16) with amk_quantize_int8.
+ * AMK_W8A16_BF16_HEAD quantizes the projections the same way and keeps the lm_head bf16 (the
+ * int8-weights reading in which only the projections shrink: the pages quote int8 weight bytes
+ * at 0.61 of bf16, a figure a bf16 head explains; gist.science explainer, Experimental
+ * Results).
  * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
  * *out receives a model handle owned by the library until amk_free.
  * Errors: INVALID_ARG (null pointers, wrong n_tensors), UNSUPPORTED (shape checks: head_dim
@@ -154,10 +160,11 @@ size_t amk_kv_cache_bytes(const amk_model* m);
 int amk_get_info(const amk_model* m, amk_info* info);
 
 /* Copies the int8 codes and fp32 row scales the library uses for canonical tensor
- * `tensor_index` (a W8A16 projection, or the lm_head index 2+9L / embed index 0 for a tied
- * model) back to host memory in canonical [rows][cols] order. codes_out: host int8
+ * `tensor_index` (a W8A16 projection, or, for AMK_W8A16, the lm_head index 2+9L / embed index 0
+ * for a tied model) back to host memory in canonical [rows][cols] order. codes_out: host int8
  * [rows*cols]; scales_out: host fp32 [rows]. Errors: INVALID_ARG for a tensor that is not
- * quantized; UNSUPPORTED for an AMK_BF16 model. */
+ * quantized (including the bf16 head of AMK_W8A16_BF16_HEAD); UNSUPPORTED for an AMK_BF16
+ * model. */
 int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes_out,
                          float* scales_out);
 

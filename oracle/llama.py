@@ -38,6 +38,7 @@ from .quant import quantize_rows_int8
 F32 = np.float32
 FMT_BF16 = 0
 FMT_W8A16 = 1
+FMT_W8A16_BF16_HEAD = 2  # W8A16 projections, lm_head kept in bf16
 
 
 # ------------------------------------------------------------------------------------------
@@ -165,12 +166,15 @@ class OracleModel:
         # the projections are independent; `threads` only spreads their construction
         # (quantization / widening) over a thread pool, the arithmetic is the same
         mats = [tensors[1 + 9 * l + o] for l in range(L) for o in (1, 2, 3, 4, 6, 7, 8)] + [lm_bits]
+        proj_fmt = FMT_BF16 if weight_format == FMT_BF16 else FMT_W8A16
+        lm_fmt = FMT_W8A16 if weight_format == FMT_W8A16 else FMT_BF16
+        fmts = [proj_fmt] * (len(mats) - 1) + [lm_fmt]
         if threads > 1:
             from concurrent.futures import ThreadPoolExecutor
             with ThreadPoolExecutor(threads) as ex:
-                lins = list(ex.map(lambda b: Linear(b, weight_format, widen_once), mats))
+                lins = list(ex.map(lambda bf: Linear(bf[0], bf[1], widen_once), zip(mats, fmts)))
         else:
-            lins = [Linear(b, weight_format, widen_once) for b in mats]
+            lins = [Linear(b, f, widen_once) for b, f in zip(mats, fmts)]
         self.layers: List[Dict[str, object]] = []
         for l in range(L):
             t = tensors[1 + 9 * l: 1 + 9 * (l + 1)]

@@ -110,6 +110,31 @@ def test_block_split_kernel_parity(fmt, monkeypatch):
     dec.close()
 
 
+@pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied"])
+def test_w8a16_with_bf16_head(which):
+    """Int8 projections with the lm_head kept bf16 (for a tied model the head reads the bf16
+    embedding table, so the model needs no quantized copy of it)."""
+    if which == "smollm2-tied":
+        shape, ctx, pre = W.SMOLLM2_135M, 40, 0
+    else:
+        shape, ctx, pre = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0), 340, 300
+    dec, orc, kv = build(shape, W.FMT_W8A16_BF16_HEAD, ctx, pre, seed0=12)
+    ref = D.Decoder(shape, W.gen_weights(shape, 12), D.AMK_W8A16, ctx)
+    assert dec.info().weight_bytes < ref.info().weight_bytes if shape.tied else \
+        dec.info().weight_bytes > ref.info().weight_bytes
+    ref.close()
+    lm_idx = 0 if shape.tied else 2 + 9 * shape.n_layers
+    with pytest.raises(D.AmkError):
+        D.amk_export_quantized(dec.model, lm_idx, shape.vocab, shape.hidden)
+    codes, scales = D.amk_export_quantized(dec.model, 2, shape.q_dim, shape.hidden)  # q_proj of layer 0
+    c_ref, s_ref = quantize_rows_int8(W.bf16_bits(W.gen_weights(shape, 12)[2]))
+    assert np.array_equal(codes, c_ref) and np.array_equal(scales.view(np.uint32), s_ref.view(np.uint32))
+    toks = W.gen_tokens(shape, 8, seed0=12)
+    res = run_teacher_forced(dec, orc, kv, shape, pre, toks[:4], 12)
+    _assert_gates(res, f"w8a16 bf16 head {which}")
+    dec.close()
+
+
 def test_determinism_and_idempotence():
     """No float atomics: repeated identical steps give bitwise-identical logits and KV entries."""
     wl = W.WORKLOADS["smollm2-135m-w8a16"]

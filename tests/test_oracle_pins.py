@@ -294,6 +294,29 @@ def test_cross_format_exact_codes():
         assert np.allclose(la, lb, rtol=1e-5, atol=1e-5)
 
 
+def test_bf16_head_format_differs_only_in_the_head():
+    """W8A16 with a bf16 lm_head: random (not exactly quantizable) projections, an lm_head of
+    k * 2^-9 rows that int8 represents exactly. Only the head differs between the two formats and
+    it computes the same products, so the logits agree to rounding; a bf16-projection model
+    (which keeps the projections unquantized) does not."""
+    shape = W.small_shape(hidden=64, n_layers=2, n_q_heads=2, n_kv_heads=1, head_dim=32, ffn=128, vocab=96,
+                          tied=False)
+    t = random_model_tensors(shape, seed=61, std=0.05)
+    g = np.random.default_rng(61)
+    k = g.integers(-127, 128, (shape.vocab, shape.hidden))
+    k[:, 0] = np.where(g.random(shape.vocab) < 0.5, 127, -127)
+    t[-1] = to_bits(k.astype(np.float32) * np.float32(2.0 ** -9))
+    a = L.OracleModel(shape, t, L.FMT_W8A16)
+    b = L.OracleModel(shape, t, L.FMT_W8A16_BF16_HEAD)
+    c = L.OracleModel(shape, t, L.FMT_BF16)
+    assert b.lm_head.fmt == L.FMT_BF16 and b.layers[1]["down"].fmt == L.FMT_W8A16
+    kva, kvb, kvc = fresh_kv(shape, 4), fresh_kv(shape, 4), fresh_kv(shape, 4)
+    for pos, tok in enumerate([3, 70, 11]):
+        la, lb, lc = a.decode_step(tok, pos, kva), b.decode_step(tok, pos, kvb), c.decode_step(tok, pos, kvc)
+        assert np.allclose(la, lb, rtol=1e-5, atol=1e-5)
+        assert np.max(np.abs(lb - lc)) > 1e-3  # the projections really are quantized
+
+
 # ------------------------------------------------------------------------------------------
 # C8 decode step-by-step == independently written full-sequence causal forward
 # ------------------------------------------------------------------------------------------
