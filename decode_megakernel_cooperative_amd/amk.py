@@ -45,7 +45,9 @@ class amk_config(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("tied_embeddings", ctypes.c_int32),
-                ("weight_format", ctypes.c_int32)]
+                ("weight_format", ctypes.c_int32), ("rope_scale_factor", ctypes.c_float),
+                ("rope_low_freq_factor", ctypes.c_float), ("rope_high_freq_factor", ctypes.c_float),
+                ("rope_original_ctx", ctypes.c_int32)]
 
 
 class amk_info(ctypes.Structure):
@@ -99,8 +101,10 @@ def amk_status_string(status: int) -> str:
 
 
 def make_config(shape, max_ctx: int, weight_format: int) -> amk_config:
+    sc = getattr(shape, "rope_scaling", None) or (0.0, 0.0, 0.0, 0)
     return amk_config(shape.hidden, shape.n_layers, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
-                      shape.vocab, max_ctx, shape.rms_eps, shape.rope_theta, int(shape.tied), weight_format)
+                      shape.vocab, max_ctx, shape.rms_eps, shape.rope_theta, int(shape.tied), weight_format,
+                      float(sc[0]), float(sc[1]), float(sc[2]), int(sc[3]))
 
 
 def amk_load_weights(cfg: amk_config, host_tensors: Sequence) -> int:

@@ -128,6 +128,10 @@ int validate_config(const amk_config* c) {
   if (c->vocab % 2) return fail(AMK_ERR_UNSUPPORTED, "vocab must be even");
   if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16 && c->weight_format != AMK_W8A16_BF16_HEAD)
     return fail(AMK_ERR_UNSUPPORTED, "weight_format");
+  if (c->rope_scale_factor > 1.0f &&
+      !(c->rope_low_freq_factor > 0.0f && c->rope_high_freq_factor > c->rope_low_freq_factor &&
+        c->rope_original_ctx > 0))
+    return fail(AMK_ERR_UNSUPPORTED, "rope scaling parameters");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(AMK_ERR_UNSUPPORTED, "rms_eps / rope_theta");
   return AMK_OK;
 }
@@ -387,13 +391,29 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   if (rc == AMK_OK) rc = upload(off_npost, npost.data(), npost.size() * 4);
   if (rc == AMK_OK) rc = upload(off_nfin, nfin.data(), nfin.size() * 4);
   if (rc == AMK_OK) {
-    // RoPE: inv_freq_i = theta^(-2i/hd) and angle = pos * inv_freq_i in double, rounded once
+    // RoPE: inv_freq_i = theta^(-2i/hd) (then the Llama-3 frequency scaling, if configured) and
+    // angle = pos * inv_freq_i in double, rounded once
     const int64_t half = hd / 2;
+    std::vector<double> inv_freq(static_cast<size_t>(half));
+    const double kPi = 3.14159265358979323846;
+    for (int64_t i = 0; i < half; ++i) {
+      double f = std::pow(static_cast<double>(c.rope_theta), -2.0 * static_cast<double>(i) / static_cast<double>(hd));
+      if (c.rope_scale_factor > 1.0f) {
+        const double factor = c.rope_scale_factor, lo = c.rope_low_freq_factor, hi = c.rope_high_freq_factor;
+        const double orig = c.rope_original_ctx, wavelen = 2.0 * kPi / f;
+        if (wavelen > orig / lo) {
+          f = f / factor;
+        } else if (wavelen >= orig / hi) {
+          const double t = (orig / wavelen - lo) / (hi - lo);
+          f = (1.0 - t) * f / factor + t * f;
+        }
+      }
+      inv_freq[static_cast<size_t>(i)] = f;
+    }
     std::vector<float> cs(static_cast<size_t>(c.max_ctx * half)), sn(cs.size());
     for (int64_t pos = 0; pos < c.max_ctx; ++pos)
       for (int64_t i = 0; i < half; ++i) {
-        const double inv = std::pow(static_cast<double>(c.rope_theta), -2.0 * static_cast<double>(i) / static_cast<double>(hd));
-        const double a = static_cast<double>(pos) * inv;
+        const double a = static_cast<double>(pos) * inv_freq[static_cast<size_t>(i)];
         cs[static_cast<size_t>(pos * half + i)] = static_cast<float>(std::cos(a));
         sn[static_cast<size_t>(pos * half + i)] = static_cast<float>(std::sin(a));
       }

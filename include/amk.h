@@ -63,6 +63,15 @@ typedef struct {
   float rope_theta;        /* RoPE base                                                      */
   int32_t tied_embeddings; /* 1: lm_head is embed_tokens                                     */
   int32_t weight_format;   /* AMK_BF16, AMK_W8A16 or AMK_W8A16_BF16_HEAD                     */
+  /* Llama-3 RoPE frequency scaling (the rule Llama 3.1 / 3.2 checkpoints declare; the pages do
+   * not describe it): rope_scale_factor <= 1 means none. Otherwise a frequency f with
+   * wavelength 2 pi / f shorter than rope_original_ctx / rope_high_freq_factor is kept, one
+   * longer than rope_original_ctx / rope_low_freq_factor becomes f / factor, and in between it
+   * moves linearly in rope_original_ctx / wavelength from f / factor to f. */
+  float rope_scale_factor;
+  float rope_low_freq_factor;
+  float rope_high_freq_factor;
+  int32_t rope_original_ctx;
 } amk_config;
 
 typedef struct amk_model amk_model; /* opaque, library-owned */

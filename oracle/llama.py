@@ -52,15 +52,38 @@ def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     return (x * r) * np.asarray(w, dtype=F32)
 
 
-def rope_tables(positions: Sequence[int] | np.ndarray, head_dim: int, theta: float):
+def scaled_inv_freq(inv_freq: np.ndarray, scaling) -> np.ndarray:
+    """Llama-3 RoPE frequency scaling (the rule Llama 3.1 / 3.2 checkpoints declare; the pages
+    do not describe it). scaling = (factor, low_freq_factor, high_freq_factor, original_ctx).
+    A frequency whose wavelength 2 pi / f is shorter than original_ctx / high_freq_factor is
+    kept; one longer than original_ctx / low_freq_factor is divided by factor; in between, the
+    result moves linearly in original_ctx / wavelength from f / factor (at low_freq_factor) to
+    f (at high_freq_factor). Float64 throughout."""
+    factor, low, high, orig = (float(v) for v in scaling)
+    out = np.empty_like(inv_freq)
+    for i, f in enumerate(inv_freq):
+        wavelen = 2.0 * np.pi / f
+        if wavelen < orig / high:
+            out[i] = f
+        elif wavelen > orig / low:
+            out[i] = f / factor
+        else:
+            t = (orig / wavelen - low) / (high - low)
+            out[i] = (1.0 - t) * f / factor + t * f
+    return out
+
+
+def rope_tables(positions: Sequence[int] | np.ndarray, head_dim: int, theta: float, scaling=None):
     """cos, sin tables [len(positions), head_dim/2] as float32.
 
-    inv_freq_i = theta^(-2i/hd) and angle = pos * inv_freq_i are evaluated in float64, then
-    cos/sin are rounded once to float32. No Llama-3 frequency scaling.
+    inv_freq_i = theta^(-2i/hd) (then the Llama-3 scaling if `scaling` is given) and
+    angle = pos * inv_freq_i are evaluated in float64, then cos/sin are rounded once to float32.
     """
     half = head_dim // 2
     i = np.arange(half, dtype=np.float64)
     inv_freq = np.power(np.float64(theta), -(2.0 * i) / head_dim)
+    if scaling is not None:
+        inv_freq = scaled_inv_freq(inv_freq, scaling)
     ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
     return np.cos(ang).astype(F32), np.sin(ang).astype(F32)
 
@@ -196,7 +219,7 @@ class OracleModel:
         hd, nq, nkv = s.head_dim, s.n_q_heads, s.n_kv_heads
         G = nq // nkv
         assert 0 <= token < s.vocab and 0 <= pos < kv.shape[3]
-        cos, sin = rope_tables([pos], hd, s.rope_theta)
+        cos, sin = rope_tables([pos], hd, s.rope_theta, s.rope_scaling)
         cos, sin = cos[0], sin[0]
         x = bf16_bits_to_f32(self.embed_bits[token]).copy()
         for l in (range(s.n_layers) if layers is None else layers):
@@ -254,7 +277,7 @@ class OracleModel:
         hd, nq, nkv = s.head_dim, s.n_q_heads, s.n_kv_heads
         G = nq // nkv
         P = len(tokens)
-        cos, sin = rope_tables(np.arange(P), hd, s.rope_theta)           # [P, hd/2]
+        cos, sin = rope_tables(np.arange(P), hd, s.rope_theta, s.rope_scaling)           # [P, hd/2]
         X = bf16_bits_to_f32(self.embed_bits[np.asarray(tokens)])         # [P, H]
         mask = np.triu(np.ones((P, P), dtype=bool), k=1)                  # True above diagonal
         for W in self.layers:

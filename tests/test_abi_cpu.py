@@ -75,6 +75,10 @@ def test_argument_validation_without_gpu():
         setattr(bad, field, value)
         st = lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h))
         assert st == A.AMK_ERR_UNSUPPORTED, (field, st, D.amk_status_string(st))
+    # inconsistent Llama-3 RoPE scaling -> UNSUPPORTED
+    bad = D.make_config(W.SMOLLM2_135M, 32, D.AMK_W8A16)
+    bad.rope_scale_factor, bad.rope_low_freq_factor, bad.rope_high_freq_factor, bad.rope_original_ctx = 8.0, 4.0, 1.0, 8192
+    assert lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h)) == A.AMK_ERR_UNSUPPORTED
     # calls on a null handle
     assert lib.amk_decode_step(None, 0, 0, None, None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_decode_step_greedy(None, None, 0, None, None, None, None) == A.AMK_ERR_INVALID_ARG

@@ -135,6 +135,19 @@ def test_w8a16_with_bf16_head(which):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+def test_llama3_rope_scaling(fmt):
+    """Llama-3.1 frequency scaling (factor 8, low 1, high 4, original context 8192) on a
+    head_dim-128 model whose frequencies fall in all three bands of the rule."""
+    shape = W.ModelShape("hd128-gqa4-scaled", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0,
+                         rope_scaling=(8.0, 1.0, 4.0, 8192))
+    dec, orc, kv = build(shape, fmt, 340, 300, seed0=10)
+    tok = W.gen_tokens(shape, 1, seed0=10)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 300, [], 12, first_token=tok, check_kv=True)
+    _assert_gates(res, f"rope scaling fmt{fmt}")
+    dec.close()
+
+
 def test_determinism_and_idempotence():
     """No float atomics: repeated identical steps give bitwise-identical logits and KV entries."""
     wl = W.WORKLOADS["smollm2-135m-w8a16"]

@@ -318,6 +318,44 @@ def test_bf16_head_format_differs_only_in_the_head():
 
 
 # ------------------------------------------------------------------------------------------
+# Llama-3 RoPE frequency scaling: bands, a worked midpoint, continuity, monotonicity
+# ------------------------------------------------------------------------------------------
+LLAMA31_SCALING = (8.0, 1.0, 4.0, 8192)
+
+
+def test_rope_scaling_bands_and_worked_midpoint():
+    hd, theta = 128, 500000.0
+    i = np.arange(hd // 2, dtype=np.float64)
+    f = np.power(theta, -(2.0 * i) / hd)
+    g = L.scaled_inv_freq(f, LLAMA31_SCALING)
+    wl = 2 * np.pi / f
+    keep, div = wl < 8192 / 4.0, wl > 8192 / 1.0
+    mid = ~keep & ~div
+    assert keep.sum() > 0 and div.sum() > 0 and mid.sum() > 0  # all three bands occur at hd 128
+    assert np.array_equal(g[keep], f[keep])
+    assert np.array_equal(g[div], f[div] / 8.0)
+    assert np.all(g[mid] > f[mid] / 8.0) and np.all(g[mid] < f[mid])
+    assert np.all(np.diff(g) <= 0)  # longer wavelengths never get a higher frequency
+    # worked value: original_ctx / wavelength halfway between the factors (2.5) gives
+    # t = 1/2, so the frequency is (1/8 + 1) / 2 = 9/16 of the unscaled one
+    fm = np.array([2 * np.pi * 2.5 / 8192])
+    assert np.isclose(L.scaled_inv_freq(fm, LLAMA31_SCALING)[0], fm[0] * 9.0 / 16.0, rtol=1e-14)
+    # continuity at both band edges
+    for edge in (8192 / 4.0, 8192 / 1.0):
+        fe = 2 * np.pi / (edge * np.array([1 - 1e-9, 1 + 1e-9]))
+        ge = L.scaled_inv_freq(fe, LLAMA31_SCALING)
+        assert np.isclose(ge[0] / fe[0], ge[1] / fe[1], rtol=1e-6)
+
+
+def test_rope_scaling_factor_one_is_plain_rope():
+    f = np.power(500000.0, -np.arange(64) / 64.0)
+    assert np.allclose(L.scaled_inv_freq(f, (1.0, 1.0, 4.0, 8192)), f, rtol=1e-15, atol=0)
+    c0, s0 = L.rope_tables([37, 900], 128, 500000.0)
+    c1, s1 = L.rope_tables([37, 900], 128, 500000.0, (1.0, 1.0, 4.0, 8192))
+    assert np.allclose(c0, c1, atol=1e-6) and np.allclose(s0, s1, atol=1e-6)
+
+
+# ------------------------------------------------------------------------------------------
 # C8 decode step-by-step == independently written full-sequence causal forward
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16])

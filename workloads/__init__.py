@@ -52,6 +52,9 @@ class ModelShape:
     tied: bool
     rope_theta: float
     rms_eps: float = 1e-5
+    # Llama-3 frequency scaling (factor, low_freq_factor, high_freq_factor, original context), or
+    # None for plain RoPE
+    rope_scaling: Optional[Tuple[float, float, float, int]] = None
 
     @property
     def q_dim(self) -> int:
