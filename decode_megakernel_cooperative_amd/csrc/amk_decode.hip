@@ -1012,29 +1012,42 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
           s[uu][h] = valid ? dot * p.attn_scale : NEG_INF;
         }
       }
+      // online softmax: new running max, rescale, and this step's weights (all zero while a row
+      // has seen no position: its max stays -inf and its sums stay 0)
+      float pe[kAttnU][GMAX];
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
         if (h >= G) continue;
         float mnew = mr[h];
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) mnew = fmaxf(mnew, s[uu][h]);
-        if (mnew == NEG_INF) continue;
         const float corr = (mr[h] == NEG_INF) ? 0.f : __expf(mr[h] - mnew);
         lr[h] *= corr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) {
-          if (gbase + uu * kWaves >= ngroups) continue;  // uniform
-          const float pe = (s[uu][h] == NEG_INF) ? 0.f : __expf(s[uu][h] - mnew);
-          lr[h] += pe;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            acc[h][2 * d] = __builtin_fmaf(pe, bf_lo(vr[uu][d]), acc[h][2 * d]);
-            acc[h][2 * d + 1] = __builtin_fmaf(pe, bf_hi(vr[uu][d]), acc[h][2 * d + 1]);
-          }
+          pe[uu][h] = (s[uu][h] == NEG_INF) ? 0.f : __expf(s[uu][h] - mnew);
+          lr[h] += pe[uu][h];
         }
         mr[h] = mnew;
+      }
+      // values: each group's V converted once, shared by the G heads
+#pragma unroll
+      for (int uu = 0; uu < kAttnU; ++uu) {
+        if (gbase + uu * kWaves >= ngroups) continue;  // uniform
+        float vf[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          vf[2 * d] = bf_lo(vr[uu][d]);
+          vf[2 * d + 1] = bf_hi(vr[uu][d]);
+        }
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          if (h >= G) continue;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pe[uu][h], vf[i], acc[h][i]);
+        }
       }
     };
 
