@@ -33,10 +33,12 @@
 //    of a pair, so the RoPE / SwiGLU / residual epilogues need no cross-wave exchange.
 //  * Attention: split-KV over (kv head, position range) units, one unit per block. The G query
 //    heads of a kv head share every K/V load. Each 16-lane row (hd 128) or 8-lane row (hd 64)
-//    scores one position per step with DPP row reductions and keeps an online softmax; rows
-//    and waves merge in registers and LDS into one tagged partial (values, max, sum) per unit;
-//    then every block of the kv head merges one slice of the head's outputs over all splits by
-//    log-sum-exp weights (DPP segmented reductions) and writes it as tagged bf16 pairs.
+//    scores one position per step with DPP row reductions and keeps an online softmax in base-2
+//    units; all rows of the block then merge in LDS (one exp2 weight per row and head) into one
+//    tagged partial (values, max, sum) per unit; then every block of the kv head merges one
+//    slice of the head's outputs over all splits by log-sum-exp weights (DPP segmented
+//    reductions) and writes it as tagged bf16 pairs. A context short enough for one split per
+//    kv head skips that second merge: the unit writes the normalised output itself.
 //  * No MFMA: batch-1 decode is a matrix-vector product, far below the MFMA ridge point.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -350,6 +352,19 @@ __device__ __forceinline__ int toff(const KParams& p, const uint64_t* buf) {
   return static_cast<int>(reinterpret_cast<const uint8_t*>(buf) - reinterpret_cast<const uint8_t*>(p.tagged));
 }
 
+// Bound of a hand-off wait, checked after its round `it`: false once the step must be abandoned.
+// The error word is read every 16 rounds (an error raised elsewhere keeps its code); the clock
+// also at round 2, so that a spin limit of one tick ends the first poll that waits at all.
+__device__ __forceinline__ bool wait_ok(const KParams& p, unsigned it, uint64_t t_start) {
+  const bool round16 = (it & 15u) == 0;
+  if (round16 && ldc(p.err) != 0u) return false;
+  if ((round16 || it == 2) && wall_clock64() - t_start > p.spin_limit) {
+    stc(p.err, kErrTimeout);
+    return false;
+  }
+  return true;
+}
+
 // Block-wide poll of nquads 16-byte quads (two tagged words each) of the tagged region: thread t
 // owns quads t + 512 b, b < VB (then further batches). When both tags of every quad of a thread
 // equal `tag` on the first read (the common case once the producers are done) visit(b, qi,
@@ -385,13 +400,7 @@ __device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_
       const uint64_t t_start = wall_clock64();
       unsigned it = 0;
       while (pend != 0u) {
-        if (((++it) & 15u) == 0) {
-          if (ldc(p.err) != 0u) return false;  // raised elsewhere: keep its code
-          if (wall_clock64() - t_start > p.spin_limit) {
-            stc(p.err, kErrTimeout);
-            return false;
-          }
-        }
+        if (!wait_ok(p, ++it, t_start)) return false;
         __builtin_amdgcn_s_sleep(2);
 #pragma unroll
         for (int b = 0; b < VB; ++b)
@@ -445,13 +454,7 @@ __device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint
       const uint64_t t_start = wall_clock64();
       unsigned it = 0;
       while (pend != 0u) {
-        if (((++it) & 15u) == 0) {
-          if (ldc(p.err) != 0u) return false;  // raised elsewhere: keep its code
-          if (wall_clock64() - t_start > p.spin_limit) {
-            stc(p.err, kErrTimeout);
-            return false;
-          }
-        }
+        if (!wait_ok(p, ++it, t_start)) return false;
         __builtin_amdgcn_s_sleep(2);
 #pragma unroll
         for (int b = 0; b < VB; ++b)
@@ -857,6 +860,18 @@ struct AttnRegs {
   i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
 };
 
+// LDS of the attention stage, in floats: every row's softmax state (a row is the LPP lanes that
+// hold one position of a wave load: [R][GMAX][RS] = values, running max, running sum, merge
+// weight, pad), then each head's block max and sum, then q of the G heads and K/V(pos).
+template <int HD, int GMAX>
+struct AttnLds {
+  static constexpr int PPW = 64 / (HD / 8);
+  static constexpr int R = kWaves * PPW;
+  static constexpr int RS = HD + 4;
+  static constexpr int kHeads = R * GMAX * RS;
+  static constexpr int kQ = kHeads + 4 * GMAX;
+};
+
 // Split-KV plan of this step: block u < nkv * S owns kv head g = u / S and positions
 // [j*T, min((j+1)*T, pos+1)) with j = u % S.
 struct AttnUnit {
@@ -927,8 +942,11 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   const int G = p.nq / p.nkv;
   const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
   const int li = lane % LPP, ri = lane / LPP, d0 = li * 8;
-  float* wp = smem;  // [kWaves][GMAX][HD + 2]
-  const float* qs = smem + kWaves * GMAX * (HD + 2);                 // q of the G heads [G][HD]
+  using Lds = AttnLds<HD, GMAX>;
+  constexpr int NR = Lds::R, RS = Lds::RS;
+  float* wp = smem;                   // row states [R][GMAX][RS]
+  float* hs = smem + Lds::kHeads;     // per head: block max, block sum
+  const float* qs = smem + Lds::kQ;   // q of the G heads [G][HD]
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(qs + G * HD);  // K(pos) [HD], V(pos) [HD]
   const AttnUnit a = attn_unit<HD>(p);
   const int g = a.g, j = a.j;
@@ -965,13 +983,16 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     };
 
     fstamp(p, layer, 0);
+    // scores are kept in base-2 units (q pre-scaled by log2(e) / sqrt(HD)), so every softmax
+    // weight is one exp2
+    const float qscale = p.attn_scale * 1.4426950408889634f;
     float qv[GMAX][8];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h < G) {
         const float* qp = qs + h * HD + d0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qv[h][i] = qp[i];
+        for (int i = 0; i < 8; ++i) qv[h][i] = qp[i] * qscale;
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) qv[h][i] = 0.f;
@@ -1009,7 +1030,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
 #pragma unroll
           for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[h][i], kf[i], dot);
           dot = group_sum<LPP>(dot);
-          s[uu][h] = valid ? dot * p.attn_scale : NEG_INF;
+          s[uu][h] = valid ? dot : NEG_INF;
         }
       }
       // online softmax: new running max, rescale, and this step's weights (all zero while a row
@@ -1021,13 +1042,13 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         float mnew = mr[h];
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) mnew = fmaxf(mnew, s[uu][h]);
-        const float corr = (mr[h] == NEG_INF) ? 0.f : __expf(mr[h] - mnew);
+        const float corr = (mr[h] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mr[h] - mnew);
         lr[h] *= corr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) {
-          pe[uu][h] = (s[uu][h] == NEG_INF) ? 0.f : __expf(s[uu][h] - mnew);
+          pe[uu][h] = (s[uu][h] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(s[uu][h] - mnew);
           lr[h] += pe[uu][h];
         }
         mr[h] = mnew;
@@ -1064,37 +1085,19 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       load(gb + 3 * step, KB, VB);
     }
 
-    // merge the rows of the wave (each row saw different positions)
-    auto merge_rows = [&](auto off_tag) {
-      constexpr int OFF = decltype(off_tag)::value;
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) continue;
-        const float mo = xor_lane<OFF>(mr[h]), lo = xor_lane<OFF>(lr[h]);
-        const float M = fmaxf(mr[h], mo);
-        const float ea = (mr[h] == NEG_INF) ? 0.f : __expf(mr[h] - M);
-        const float eb = (mo == NEG_INF) ? 0.f : __expf(mo - M);
-        lr[h] = lr[h] * ea + lo * eb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * ea + xor_lane<OFF>(acc[h][i]) * eb;
-        mr[h] = M;
-      }
-    };
+    // every row's state into LDS (each row saw its own positions); rows that saw none hold
+    // max -inf and zero sums
     fstamp(p, layer, 2);
-    if (LPP == 8) merge_rows(std::integral_constant<int, 8>{});
-    merge_rows(std::integral_constant<int, 16>{});
-    merge_rows(std::integral_constant<int, 32>{});
-    if (ri == 0) {
+    float* row = wp + (wave * Lds::PPW + ri) * GMAX * RS;
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) continue;
-        float* dst = wp + (wave * GMAX + h) * (HD + 2);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dst[d0 + i] = acc[h][i];
-        if (li == 0) {
-          dst[HD] = mr[h];
-          dst[HD + 1] = lr[h];
-        }
+    for (int h = 0; h < GMAX; ++h) {
+      if (h >= G) continue;
+      float* dst = row + h * RS + d0;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      if (li == 0) {
+        row[h * RS + HD] = mr[h];
+        row[h * RS + HD + 1] = lr[h];
       }
     }
   }
@@ -1102,27 +1105,51 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   fstamp(p, layer, 3);
   if (!a.active) return;
 
-  // merge the waves of the block -> this unit's partial (values, max, sum) as tagged words
-  const uint32_t tpart = tag_of(p, layer, kTagPart);
-  for (int t = tid; t < G * HD; t += kThreads) {
-    const int h = t / HD, d = t - h * HD;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wp[(w * GMAX + h) * (HD + 2) + HD]);
-    float A = 0.f, Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* src = wp + (w * GMAX + h) * (HD + 2);
-      const float mw = src[HD];
-      const float e = (mw == NEG_INF) ? 0.f : __expf(mw - M);
-      A += src[d] * e;
-      Lsum += src[HD + 1] * e;
+  // wave h < G: the head's block max M over the R rows, each row's weight 2^(m - M) and the
+  // block sum of the rows' sums under those weights
+  if (wave < G) {
+    const int h = wave;
+    float* rp = wp + (min(lane, NR - 1) * GMAX + h) * RS;
+    const float m = lane < NR ? rp[HD] : NEG_INF;
+    const float M = wave_max(m);  // finite: row 0 of wave 0 holds the unit's first position
+    const float w = (m == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    const float Ls = wave_sum(lane < NR ? rp[HD + 1] * w : 0.f);
+    if (lane < NR) rp[HD + 2] = w;
+    if (lane == 0) {
+      hs[2 * h] = M;
+      hs[2 * h + 1] = Ls;
     }
-    uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
-    st_tag(dst + d, __float_as_uint(A), tpart);
-    if (d == 0) {
-      st_tag(dst + HD, __float_as_uint(M), tpart);
-      st_tag(dst + HD + 1, __float_as_uint(Lsum), tpart);
+  }
+  wg_barrier();
+
+  // one pair of output dims of one head per thread: the weighted sum over the rows, then either
+  // this unit's tagged partial (values, max, sum) or, for a single split, the attention output
+  const uint32_t tpart = tag_of(p, layer, kTagPart), to_tag = tag_of(p, layer, kTagO);
+  for (int t = tid; t < G * HD / 2; t += kThreads) {
+    const int h = t / (HD / 2), d = 2 * (t - h * (HD / 2));
+    const float* rp = wp + h * RS;
+    float A0 = 0.f, A1 = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < NR; ++r) {
+      const float w = rp[r * GMAX * RS + HD + 2];
+      const float2 v = *reinterpret_cast<const float2*>(rp + r * GMAX * RS + d);
+      A0 = __builtin_fmaf(v.x, w, A0);
+      A1 = __builtin_fmaf(v.y, w, A1);
+    }
+    const float M = hs[2 * h], Ls = hs[2 * h + 1];
+    if (S == 1) {
+      const float inv = 1.0f / Ls;
+      st_tag(p.to + ((g * G + h) * HD + d) / 2,
+             static_cast<uint32_t>(f32_to_bf16(A0 * inv)) | (static_cast<uint32_t>(f32_to_bf16(A1 * inv)) << 16),
+             to_tag);
+    } else {
+      uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
+      st_tag(dst + d, __float_as_uint(A0), tpart);
+      st_tag(dst + d + 1, __float_as_uint(A1), tpart);
+      if (d == 0) {
+        st_tag(dst + HD, __float_as_uint(M), tpart);
+        st_tag(dst + HD + 1, __float_as_uint(Ls), tpart);
+      }
     }
   }
 }
@@ -1134,7 +1161,7 @@ template <int HD>
 __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int layer) {
   const float NEG_INF = -__builtin_inff();
   const AttnUnit a = attn_unit<HD>(p);
-  if (!a.active) return true;
+  if (!a.active || p.S == 1) return true;  // a single split wrote the output itself
   const int G = p.nq / p.nkv, S = p.S, g = a.g, j = a.j;
   const int tid = opaque(threadIdx.x);
   const int nw = G * HD / 2;  // output words of the kv head (2 bf16 each)
@@ -1173,7 +1200,7 @@ __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int laye
     const bool v = wd < w1 && sp < S;
     const float mj = v ? mv[r] : NEG_INF;
     const float M = seg_max(mj, SP);
-    const float e = (mj == NEG_INF) ? 0.f : __expf(mj - M);
+    const float e = (mj == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mj - M);  // base-2 maxima
     const float Ls = seg_sum(v ? lv[r] * e : 0.f, SP);
     const float wgt = e * (1.0f / Ls);
     const float o0 = seg_sum(v ? av[r][0] * wgt : 0.f, SP);
@@ -1308,7 +1335,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   };
   stamp();
   float* xs = smem;                                  // GEMV input vector (swizzled)
-  float* qs = smem + kWaves * GMAX * (HD + 2);       // attention: q, K/V(pos)
+  float* qs = smem + AttnLds<HD, GMAX>::kQ;          // attention: q, K/V(pos)
   const int H = p.H, L = p.L;
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;

@@ -278,8 +278,10 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     m->lds_bytes = static_cast<int>(4 * o);
     m->kernel = amk_stream_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
   } else {
-    // attention: the waves' softmax states, then q of the G heads and K/V(pos)
-    const int64_t attn_f = static_cast<int64_t>(amk::kWaves) * m->gmax * (hd + 2) + G * hd + hd;
+    // attention: every row's softmax state (a row: the lanes holding one position of a wave's
+    // load, 512 / hd rows per wave), each head's max and sum, then q of the G heads and K/V(pos)
+    const int64_t rows = static_cast<int64_t>(amk::kWaves) * (512 / hd);
+    const int64_t attn_f = rows * m->gmax * (hd + 4) + 4 * m->gmax + G * hd + hd;
     m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
     m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
   }
@@ -482,8 +484,12 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   k.pos = pos;
   const int ctx = pos + 1;
   // split-KV plan: at most s_cap splits per kv head (one attention unit per block), at least
-  // 16 positions per split
+  // 16 positions per split. The wave kernel keeps a context that one block covers in a single
+  // pipeline step (8 waves x U groups x 512 / head_dim positions) in one split, which then writes
+  // the attention output itself, with no merge hand-off.
+  const int tstep = amk::kWaves * (m->gmax > 4 ? 2 : 4) * (512 / m->cfg.head_dim);
   int T = std::max(16, (ctx + m->s_cap - 1) / m->s_cap);
+  if (!m->stream && ctx <= tstep) T = tstep;
   k.T = T;
   k.S = (ctx + T - 1) / T;
   k.kv = static_cast<uint16_t*>(kv_cache);
