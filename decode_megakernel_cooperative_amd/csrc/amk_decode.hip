@@ -1122,20 +1122,42 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   }
   wg_barrier();
 
-  // one pair of output dims of one head per thread: the weighted sum over the rows, then either
-  // this unit's tagged partial (values, max, sum) or, for a single split, the attention output
+  // The weighted sum over the rows of each pair of output dims of each head: NS lanes of a quad
+  // take every NS-th row (eight rows per batch of LDS reads) and add their sums by DPP. The
+  // quad's first lane then writes this unit's tagged partial (values, max, sum) or, for a single
+  // split, the attention output.
+  const int npair = G * HD / 2;
+  const int NS = npair * 4 <= kThreads ? 4 : (npair * 2 <= kThreads ? 2 : 1);  // uniform
   const uint32_t tpart = tag_of(p, layer, kTagPart), to_tag = tag_of(p, layer, kTagO);
-  for (int t = tid; t < G * HD / 2; t += kThreads) {
-    const int h = t / (HD / 2), d = 2 * (t - h * (HD / 2));
+  for (int t = tid; t < npair * NS; t += kThreads) {  // NS divides npair * NS: quads stay whole
+    const int pi = t / NS, sub = t - pi * NS;
+    const int h = pi / (HD / 2), d = 2 * (pi - h * (HD / 2));
     const float* rp = wp + h * RS;
     float A0 = 0.f, A1 = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < NR; ++r) {
-      const float w = rp[r * GMAX * RS + HD + 2];
-      const float2 v = *reinterpret_cast<const float2*>(rp + r * GMAX * RS + d);
-      A0 = __builtin_fmaf(v.x, w, A0);
-      A1 = __builtin_fmaf(v.y, w, A1);
+    for (int r0 = sub; r0 < NR; r0 += 8 * NS) {  // NR / NS is a multiple of 8
+      float w[8];
+      float2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* q = rp + (r0 + k * NS) * GMAX * RS;
+        w[k] = q[HD + 2];
+        v[k] = *reinterpret_cast<const float2*>(q + d);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        A0 = __builtin_fmaf(v[k].x, w[k], A0);
+        A1 = __builtin_fmaf(v[k].y, w[k], A1);
+      }
     }
+    if (NS >= 2) {
+      A0 += dpp<0xB1>(A0);
+      A1 += dpp<0xB1>(A1);
+    }
+    if (NS >= 4) {
+      A0 += dpp<0x4E>(A0);
+      A1 += dpp<0x4E>(A1);
+    }
+    if (sub != 0) continue;
     const float M = hs[2 * h], Ls = hs[2 * h + 1];
     if (S == 1) {
       const float inv = 1.0f / Ls;
