@@ -24,7 +24,9 @@ activations are rounded to bf16 exactly at GEMV inputs and at KV-cache storage, 
 softmax, gate/up and logits stay fp32; the W8A16 GEMV is s_n * sum_k q_nk x_k with the row
 scale applied once after the fp32 sum; RoPE angles are computed in float64 and rounded to
 fp32 cos/sin, with no frequency scaling; all seven per-layer projections and the lm_head are
-int8 under W8A16 while the embedding gather reads the bf16 table.
+int8 under W8A16 while the embedding gather reads the bf16 table. W4A16 quantizes the seven
+projections to int4 codes with the same per-row rule (scale max|row| / 7) and keeps the lm_head
+bf16; its GEMV is the same s_n * sum_k q_nk x_k.
 """
 from __future__ import annotations
 
@@ -33,12 +35,13 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 from .numerics import bf16_bits_to_f32, f32_to_bf16_bits, round_bf16
-from .quant import quantize_rows_int8
+from .quant import quantize_rows_int4, quantize_rows_int8
 
 F32 = np.float32
 FMT_BF16 = 0
 FMT_W8A16 = 1
 FMT_W8A16_BF16_HEAD = 2  # W8A16 projections, lm_head kept in bf16
+FMT_W4A16 = 3            # int4 projections (per-row scale), lm_head kept in bf16
 
 
 # ------------------------------------------------------------------------------------------
@@ -124,7 +127,8 @@ def gemv(W: "Linear", x: np.ndarray) -> np.ndarray:
 # weights
 # ------------------------------------------------------------------------------------------
 class Linear:
-    """A [rows, cols] projection applied as y = W x (bf16 weights) or y = s * (Q x) (int8)."""
+    """A [rows, cols] projection applied as y = W x (bf16 weights) or y = s * (Q x) (int8 or int4
+    codes, one fp32 scale per row)."""
 
     BLOCK = 8192
 
@@ -134,8 +138,9 @@ class Linear:
         self.fmt = fmt
         self.codes = self.scales = self.bits = None
         self._f32 = None
-        if fmt == FMT_W8A16:
-            self.codes, self.scales = quantize_rows_int8(bits)
+        if fmt in (FMT_W8A16, FMT_W4A16):
+            quantize = quantize_rows_int8 if fmt == FMT_W8A16 else quantize_rows_int4
+            self.codes, self.scales = quantize(bits)
             if widen_once:
                 self._f32 = self.codes.astype(F32)
         else:
@@ -146,7 +151,7 @@ class Linear:
     def _block(self, r0: int, r1: int) -> np.ndarray:
         if self._f32 is not None:
             return self._f32[r0:r1]
-        if self.fmt == FMT_W8A16:
+        if self.codes is not None:
             return self.codes[r0:r1].astype(F32)
         return bf16_bits_to_f32(self.bits[r0:r1])
 
@@ -160,7 +165,7 @@ class Linear:
             r1 = min(self.rows, r0 + self.BLOCK)
             W = self._block(r0, r1).astype(accum, copy=False)
             acc = xa @ W.T
-            if self.fmt == FMT_W8A16:
+            if self.codes is not None:
                 acc = acc * self.scales[r0:r1].astype(accum)
             y[..., r0:r1] = acc
         return y
@@ -189,7 +194,8 @@ class OracleModel:
         # the projections are independent; `threads` only spreads their construction
         # (quantization / widening) over a thread pool, the arithmetic is the same
         mats = [tensors[1 + 9 * l + o] for l in range(L) for o in (1, 2, 3, 4, 6, 7, 8)] + [lm_bits]
-        proj_fmt = FMT_BF16 if weight_format == FMT_BF16 else FMT_W8A16
+        proj_fmt = {FMT_BF16: FMT_BF16, FMT_W8A16: FMT_W8A16, FMT_W8A16_BF16_HEAD: FMT_W8A16,
+                    FMT_W4A16: FMT_W4A16}[weight_format]
         lm_fmt = FMT_W8A16 if weight_format == FMT_W8A16 else FMT_BF16
         fmts = [proj_fmt] * (len(mats) - 1) + [lm_fmt]
         if threads > 1:

@@ -1,4 +1,5 @@
-"""Symmetric per-output-row int8 weight quantizer (W8A16) — oracle, test infrastructure only.
+"""Symmetric per-output-row int8 (W8A16) and int4 (W4A16) weight quantizers — oracle, test
+infrastructure only.
 
 The pages report a search-found int8 weight-only (W8A16) megakernel that is greedy-lossless
 (AutoMegaKernel paper index, Abstract; gist.science explainer, Technical Summary > Key
@@ -13,6 +14,15 @@ are common enough at these shapes that the choice changes bytes:
     amax_n == 0  ->  s_n = 0, q_n = 0
 
 Dequantized weight: w'_nk = q_nk * s_n; a W8A16 GEMV row is s_n * sum_k q_nk * x_k.
+
+int4 (W4A16). The pages list an int4 weight-only variant as lossy with 2.42x less weight traffic
+than bf16 (gist.science explainer, Technical Summary > Key Contributions) and give no format.
+The reading used here is the same rule at four bits: symmetric per output row, s_n =
+fp32(amax_n / 7) by IEEE division, q_nk = clamp(round_half_even(fp32(w_nk / s_n)), -7, 7), a
+zero row gives s_n = 0 and q_n = 0. With the lm_head (and a tied embedding) kept in bf16 this
+streams 1 / 2.44 of the bf16 weight bytes for SmolLM2-135M and for Llama-3.2-1B, which matches
+the pages' figure to its precision. Codes are stored two per byte on the GPU side; here they are
+kept one per int8.
 """
 import numpy as np
 
@@ -23,17 +33,31 @@ def quantize_rows_int8(w_bits: np.ndarray, block_rows: int = 4096):
     """bf16 matrix (uint16 patterns, [rows, cols]) -> (int8 codes [rows, cols], fp32 scales [rows])."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     assert w_bits.ndim == 2
-    return _quantize(w_bits, bf16_bits_to_f32, block_rows)
+    return _quantize(w_bits, bf16_bits_to_f32, block_rows, 127)
 
 
 def quantize_rows_int8_f32(w: np.ndarray, block_rows: int = 4096):
     """The same quantizer applied to fp32 rows (used to re-quantize dequantized weights)."""
     w = np.asarray(w, dtype=np.float32)
     assert w.ndim == 2
-    return _quantize(w, lambda a: a, block_rows)
+    return _quantize(w, lambda a: a, block_rows, 127)
 
 
-def _quantize(src: np.ndarray, widen, block_rows: int):
+def quantize_rows_int4(w_bits: np.ndarray, block_rows: int = 4096):
+    """bf16 matrix (uint16 patterns) -> (codes in [-7, 7] as int8 [rows, cols], fp32 scales [rows])."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    assert w_bits.ndim == 2
+    return _quantize(w_bits, bf16_bits_to_f32, block_rows, 7)
+
+
+def quantize_rows_int4_f32(w: np.ndarray, block_rows: int = 4096):
+    """The int4 quantizer applied to fp32 rows (used to re-quantize dequantized weights)."""
+    w = np.asarray(w, dtype=np.float32)
+    assert w.ndim == 2
+    return _quantize(w, lambda a: a, block_rows, 7)
+
+
+def _quantize(src: np.ndarray, widen, block_rows: int, qmax: int):
     rows, cols = src.shape
     codes = np.empty((rows, cols), dtype=np.int8)
     scales = np.empty(rows, dtype=np.float32)
@@ -41,11 +65,11 @@ def _quantize(src: np.ndarray, widen, block_rows: int):
         r1 = min(rows, r0 + block_rows)
         w = widen(src[r0:r1])
         amax = np.max(np.abs(w), axis=1)
-        s = (amax / np.float32(127.0)).astype(np.float32)
+        s = (amax / np.float32(qmax)).astype(np.float32)
         zero = s == 0
         s_safe = np.where(zero, np.float32(1.0), s).astype(np.float32)
         q = np.rint(w / s_safe[:, None])  # float32 / float32 stays float32; rint = half-even
-        q = np.clip(q, -127, 127)
+        q = np.clip(q, -qmax, qmax)
         q[zero] = 0
         codes[r0:r1] = q.astype(np.int8)
         scales[r0:r1] = np.where(zero, np.float32(0.0), s)

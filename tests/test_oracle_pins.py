@@ -18,7 +18,8 @@ import torch
 import oracle
 from oracle import llama as L
 from oracle.numerics import bf16_bits_to_f32, f32_to_bf16_bits, round_bf16
-from oracle.quant import quantize_rows_int8, quantize_rows_int8_f32, dequantize_rows
+from oracle.quant import (dequantize_rows, quantize_rows_int4, quantize_rows_int4_f32, quantize_rows_int8,
+                          quantize_rows_int8_f32)
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -60,7 +61,7 @@ def test_bf16_round_matches_torch():
 # C1 GEMV: brute force in float64 double loops on tiny non-square shapes
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("rows,cols", [(7, 13), (5, 64), (16, 33)])
-@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16])
+@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16, L.FMT_W4A16])
 def test_gemv_brute_force(rows, cols, fmt):
     wb = rng_bf16((rows, cols), 0.5, rows * cols + fmt)
     x = round_bf16(np.random.default_rng(1).standard_normal(cols).astype(np.float32))
@@ -68,13 +69,14 @@ def test_gemv_brute_force(rows, cols, fmt):
     y = lin.apply(x)
     assert y.shape == (rows,)
     w = bf16_bits_to_f32(wb).astype(np.float64)
-    if fmt == L.FMT_W8A16:
+    if fmt != L.FMT_BF16:
         codes, scales = lin.codes.astype(np.float64), lin.scales.astype(np.float64)
+        assert np.max(np.abs(codes)) == (127 if fmt == L.FMT_W8A16 else 7)
     for r in range(rows):
         terms = [(codes[r, c] if fmt else w[r, c]) * float(x[c]) for c in range(cols)]
         exact = sum(terms)
         absum = sum(abs(t) for t in terms)
-        if fmt == L.FMT_W8A16:
+        if fmt != L.FMT_BF16:
             exact *= scales[r]
             absum *= scales[r]
         bound = (cols + 1) * 2.0 ** -24 * absum + 1e-30
@@ -216,6 +218,32 @@ def test_quantizer_invariants_and_round_trip():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_int4_quantizer_worked_rows():
+    d = json.load(open(os.path.join(GOLDEN, "quant4_tie_row.json")))
+    for row in d["rows"]:
+        wb = to_bits(np.array([row["w_float"]], np.float32))
+        assert np.array_equal(bf16_bits_to_f32(wb)[0], np.array(row["w_float"], np.float32))  # exact in bf16
+        codes, scales = quantize_rows_int4(wb)
+        assert codes[0].tolist() == row["codes"], row["why"]
+        assert scales[0] == np.float32(row["scale"])
+
+
+def test_int4_quantizer_invariants_and_round_trip():
+    for cols in (576, 2048, 4096):
+        wb = rng_bf16((256, cols), 0.02, cols + 1)
+        codes, s = quantize_rows_int4(wb)
+        w = bf16_bits_to_f32(wb)
+        assert np.all(np.max(np.abs(codes.astype(np.int32)), axis=1) == 7)
+        assert codes.min() >= -7 and codes.max() <= 7
+        assert np.all(np.abs(w - dequantize_rows(codes, s)) <= s[:, None] * (0.5 + 1e-5))
+        c2, s2 = quantize_rows_int4_f32(dequantize_rows(codes, s))
+        assert np.array_equal(c2, codes) and np.array_equal(s2, s)
+        # the int8 and int4 rules differ only in the code range: 127 / 7 of the int4 scale is
+        # the int8 scale up to one rounding
+        c8, s8 = quantize_rows_int8(wb)
+        assert np.allclose(s8 * np.float32(127 / 7), s, rtol=3e-7)
+
+
 # ------------------------------------------------------------------------------------------
 # small-model helpers
 # ------------------------------------------------------------------------------------------
@@ -294,6 +322,41 @@ def test_cross_format_exact_codes():
         assert np.allclose(la, lb, rtol=1e-5, atol=1e-5)
 
 
+def test_int4_exact_codes_match_bf16_model():
+    """Projections of k * 2^-9 with |k| <= 7 and one |k| = 7 per row are exact int4 codes with
+    s = 2^-9, so the W4A16 model equals the bf16 model on the same tensors to rounding. The
+    lm_head stays bf16 under W4A16 (its rows here are ordinary random values)."""
+    shape = W.small_shape(hidden=64, n_layers=2, n_q_heads=2, n_kv_heads=1, head_dim=32, ffn=128, vocab=96,
+                          tied=False)
+    g = np.random.default_rng(17)
+    tensors = []
+    for i, (name, dims, kind) in enumerate(W.tensor_specs(shape)):
+        if kind == "norm":
+            tensors.append(to_bits(np.ones(dims, np.float32)))
+        elif i == len(W.tensor_specs(shape)) - 1 or i == 0:  # lm_head, embedding: plain bf16
+            tensors.append(rng_bf16(dims, 0.05, 170 + i))
+        else:
+            k = g.integers(-7, 8, dims)
+            k[:, 0] = np.where(g.random(dims[0]) < 0.5, 7, -7)
+            tensors.append(to_bits(k.astype(np.float32) * np.float32(2.0 ** -9)))
+    a = L.OracleModel(shape, tensors, L.FMT_BF16)
+    b = L.OracleModel(shape, tensors, L.FMT_W4A16)
+    lin = b.layers[1]["gate"]
+    assert lin.fmt == L.FMT_W4A16 and b.lm_head.fmt == L.FMT_BF16
+    assert np.all(lin.scales == np.float32(2.0 ** -9))
+    assert np.array_equal(lin.codes.astype(np.float32) * np.float32(2.0 ** -9), bf16_bits_to_f32(tensors[1 + 9 + 6]))
+    kva, kvb = fresh_kv(shape, 4), fresh_kv(shape, 4)
+    for pos, tok in enumerate([1, 50, 95]):
+        la = a.decode_step(tok, pos, kva)
+        lb = b.decode_step(tok, pos, kvb)
+        assert np.allclose(la, lb, rtol=1e-5, atol=1e-5)
+    # on ordinary random weights int4 is lossy: the logits move well beyond rounding
+    t = random_model_tensors(shape, seed=18, std=0.05)
+    a, b = L.OracleModel(shape, t, L.FMT_BF16), L.OracleModel(shape, t, L.FMT_W4A16)
+    kva, kvb = fresh_kv(shape, 4), fresh_kv(shape, 4)
+    assert np.max(np.abs(a.decode_step(3, 0, kva) - b.decode_step(3, 0, kvb))) > 1e-2
+
+
 def test_bf16_head_format_differs_only_in_the_head():
     """W8A16 with a bf16 lm_head: random (not exactly quantizable) projections, an lm_head of
     k * 2^-9 rows that int8 represents exactly. Only the head differs between the two formats and
@@ -358,7 +421,7 @@ def test_rope_scaling_factor_one_is_plain_rope():
 # ------------------------------------------------------------------------------------------
 # C8 decode step-by-step == independently written full-sequence causal forward
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16])
+@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16, L.FMT_W4A16])
 def test_decode_equals_prefill(fmt):
     shape = W.small_shape(hidden=64, n_layers=3, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=96, vocab=200)
     t = random_model_tensors(shape, seed=21, std=0.1)

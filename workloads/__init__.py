@@ -37,6 +37,7 @@ WEIGHT_STD = 0.02
 FMT_BF16 = 0
 FMT_W8A16 = 1
 FMT_W8A16_BF16_HEAD = 2  # W8A16 projections, bf16 lm_head
+FMT_W4A16 = 3            # int4 per-row projections, bf16 lm_head
 
 
 @dataclass(frozen=True)
@@ -98,7 +99,8 @@ class Workload:
 
     @property
     def fmt_name(self) -> str:
-        return {FMT_BF16: "bf16", FMT_W8A16: "w8a16", FMT_W8A16_BF16_HEAD: "w8a16-bf16head"}[self.weight_format]
+        return {FMT_BF16: "bf16", FMT_W8A16: "w8a16", FMT_W8A16_BF16_HEAD: "w8a16-bf16head",
+                FMT_W4A16: "w4a16"}[self.weight_format]
 
 
 WORKLOADS = {
@@ -110,6 +112,9 @@ WORKLOADS = {
     # the pages' "0.61x the bytes" reading: the same W8A16 model with the lm_head kept in bf16
     "llama3-8b-w8a16hb-ctx4096": Workload("llama3-8b-w8a16hb-ctx4096", LLAMA3_8B, FMT_W8A16_BF16_HEAD, 0, 4096, 128),
     "llama3-8b-w8a16-ctx32768": Workload("llama3-8b-w8a16-ctx32768", LLAMA3_8B, FMT_W8A16, 0, 32768, 64),
+    # the pages' int4 weight-only variant (lossy, 2.42x less weight traffic than bf16)
+    "smollm2-135m-w4a16": Workload("smollm2-135m-w4a16", SMOLLM2_135M, FMT_W4A16, 64, 0, 128),
+    "llama3-8b-w4a16-ctx4096": Workload("llama3-8b-w4a16-ctx4096", LLAMA3_8B, FMT_W4A16, 0, 4096, 128),
 }
 
 
