@@ -26,11 +26,12 @@ AMK_ERR_OOM = -6
 AMK_BF16 = 0
 AMK_W8A16 = 1
 AMK_W8A16_BF16_HEAD = 2
+AMK_W4A16 = 3
 AMK_KERNEL_WAVE = 0
 AMK_KERNEL_BLOCK = 1
 
 EXPORTED = ("amk_load_weights", "amk_decode_step", "amk_decode_step_greedy", "amk_sync", "amk_kv_cache_bytes", "amk_get_info",
-            "amk_export_quantized", "amk_quantize_int8", "amk_bench_barrier", "amk_set_spin_limit",
+            "amk_export_quantized", "amk_quantize_int8", "amk_quantize_int4", "amk_bench_barrier", "amk_set_spin_limit",
             "amk_set_trace", "amk_free", "amk_status_string")
 
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.amk_get_info.argtypes = [vp, ctypes.POINTER(amk_info)]
         L.amk_export_quantized.argtypes = [vp, i32, vp, vp]
         L.amk_quantize_int8.argtypes = [vp, i64, i64, vp, vp]
+        L.amk_quantize_int4.argtypes = [vp, i64, i64, vp, vp]
         L.amk_bench_barrier.argtypes = [i32, ctypes.POINTER(ctypes.c_float)]
         L.amk_set_spin_limit.argtypes = [vp, ctypes.c_uint64]
         L.amk_set_trace.argtypes = [vp, vp, i32]
@@ -179,6 +181,15 @@ def amk_quantize_int8(w_bits: np.ndarray):
     codes = np.empty((rows, cols), dtype=np.int8)
     scales = np.empty(rows, dtype=np.float32)
     _check(lib().amk_quantize_int8(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
+
+
+def amk_quantize_int4(w_bits: np.ndarray):
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scales = np.empty(rows, dtype=np.float32)
+    _check(lib().amk_quantize_int4(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data))
     return codes, scales
 
 

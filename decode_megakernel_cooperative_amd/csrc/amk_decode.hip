@@ -28,6 +28,8 @@
 //    four 16-byte LDS reads of a lane per weight chunk are bank-conflict free.
 //  * W8A16: int8 codes convert with one v_cvt_f32_i32 (SDWA byte select, sign extend) per
 //    weight and feed an fp32 FMA; the per-row fp32 scale multiplies the wave-reduced sum.
+//    W4A16: two codes per byte; each converts with one v_cvt_off_f32_i4 on an SDWA byte select
+//    of the dword or of the dword shifted right by 4 (2.125 VALU per weight with the FMA).
 //  * Row pairs: rows are packed at load time so that rows i and i + hd/2 of one head (a RoPE
 //    pair) and rows n of gate and up (a SwiGLU pair) are adjacent; one wave computes both rows
 //    of a pair, so the RoPE / SwiGLU / residual epilogues need no cross-wave exchange.
@@ -292,8 +294,9 @@ struct GridBarrier {
 // weight formats and the LDS layout of a GEMV input vector
 // ------------------------------------------------------------------------------------------
 template <int FMT> struct Fmt;
-template <> struct Fmt<0> { static constexpr int WB = 2, CW = 512, LC = 8; };   // bf16
-template <> struct Fmt<1> { static constexpr int WB = 1, CW = 1024, LC = 16; };  // int8
+template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8; };  // bf16
+template <> struct Fmt<1> { static constexpr int BITS = 8, CW = 1024, LC = 16; };  // int8
+template <> struct Fmt<2> { static constexpr int BITS = 4, CW = 2048, LC = 32; };  // int4
 // A 1 KB weight chunk covers CW columns; lane L owns LC consecutive columns (16 bytes).
 // Column e is stored at chunk*CW + (k/4)*256 + L*4 + k%4, k = e's index inside the lane, so
 // the lane's k/4-th float4 sits at a 16-byte lane stride: conflict-free ds_read_b128.
@@ -599,7 +602,7 @@ __device__ __forceinline__ int pidx(const GemvPlan& g, int k) { return g.st0 + k
 template <int FMT>
 __device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave, int unit) {
   GemvPlan g;
-  g.RB = K * Fmt<FMT>::WB;
+  g.RB = K * Fmt<FMT>::BITS / 8;
   g.nch = (g.RB + 1023) >> 10;
   g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
   const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
@@ -631,13 +634,59 @@ struct Cursor {
   }
 };
 
+// Signed int4 code in bits 3:0 of byte B of v, times 1/16 (v_cvt_off_f32_i4 on an SDWA byte
+// select: one VALU op per code).
+template <int B>
+__device__ __forceinline__ float i4_at(int v) {
+  float r;
+  if (B == 0) r = __builtin_amdgcn_cvt_off_f32_i4(v);
+  else if (B == 1) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  else if (B == 2) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  else asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
+}
+
 template <int FMT>
 __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const float* __restrict__ xl,
                                           float& a0, float& a1) {
-  if (FMT == 1) {
+  // All activation reads of the slot are issued before the first FMA, so the slot waits for LDS
+  // once instead of once per float4.
+  if (FMT == 2) {
+    // dword d holds columns 8d .. 8d + 7, column 8d + i in bits 4i .. 4i + 3; codes arrive as
+    // q / 16 (the row scale carries the 16)
+    f32x4 xv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xv[k] = *reinterpret_cast<const f32x4*>(xl + k * 256);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(xl + d * 256);
+      const f32x4 xa = xv[2 * d], xb = xv[2 * d + 1];
+      const int u0 = w0[d], u1 = w1[d];
+      const int h0 = static_cast<int>(static_cast<uint32_t>(u0) >> 4);
+      const int h1 = static_cast<int>(static_cast<uint32_t>(u1) >> 4);
+      a0 = __builtin_fmaf(i4_at<0>(u0), xa[0], a0);
+      a1 = __builtin_fmaf(i4_at<0>(u1), xa[0], a1);
+      a0 = __builtin_fmaf(i4_at<0>(h0), xa[1], a0);
+      a1 = __builtin_fmaf(i4_at<0>(h1), xa[1], a1);
+      a0 = __builtin_fmaf(i4_at<1>(u0), xa[2], a0);
+      a1 = __builtin_fmaf(i4_at<1>(u1), xa[2], a1);
+      a0 = __builtin_fmaf(i4_at<1>(h0), xa[3], a0);
+      a1 = __builtin_fmaf(i4_at<1>(h1), xa[3], a1);
+      a0 = __builtin_fmaf(i4_at<2>(u0), xb[0], a0);
+      a1 = __builtin_fmaf(i4_at<2>(u1), xb[0], a1);
+      a0 = __builtin_fmaf(i4_at<2>(h0), xb[1], a0);
+      a1 = __builtin_fmaf(i4_at<2>(h1), xb[1], a1);
+      a0 = __builtin_fmaf(i4_at<3>(u0), xb[2], a0);
+      a1 = __builtin_fmaf(i4_at<3>(u1), xb[2], a1);
+      a0 = __builtin_fmaf(i4_at<3>(h0), xb[3], a0);
+      a1 = __builtin_fmaf(i4_at<3>(h1), xb[3], a1);
+    }
+  } else if (FMT == 1) {
+    f32x4 xv[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xv[d] = *reinterpret_cast<const f32x4*>(xl + d * 256);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x4 x = xv[d];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         a0 = __builtin_fmaf(i8_to_f32(w0[d], k), x[k], a0);
@@ -645,9 +694,12 @@ __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const 
       }
     }
   } else {
+    f32x4 xv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xv[h] = *reinterpret_cast<const f32x4*>(xl + h * 256);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(xl + h * 256);
+      const f32x4 x = xv[h];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const int u0 = w0[2 * h + d], u1 = w1[2 * h + d];
@@ -661,7 +713,7 @@ __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const 
 }
 
 // Per-pair operands for a window of 32 pairs: lane j holds the value for row j & 1 of the
-// window's pair j / 2: A = W8A16 row scale, B = residual input (EPI_RESID) or RoPE cos
+// window's pair j / 2: A = the row scale of int8 / int4 weights, B = residual input (EPI_RESID) or RoPE cos
 // (even j) / sin (odd j) of the pair (EPI_QKV).
 template <int FMT, int EPI>
 __device__ __forceinline__ void load_window(const KParams& p, const float* __restrict__ Sc, const GemvPlan& g,
@@ -673,6 +725,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   B = 0.f;
   if (k < g.pb) {
     if (FMT == 1) A = Sc[row];
+    if (FMT == 2) A = Sc[row] * 16.f;  // exact: the int4 products arrive as q / 16
     if (EPI == EPI_RESID) {
       B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
                            : ld_payload(p.tx + row);
@@ -778,7 +831,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       float y0 = wave_sum(acc0), y1 = wave_sum(acc1);
       acc0 = acc1 = 0.f;
       const int j = 2 * c.k;
-      if (FMT == 1) {
+      if (FMT != 0) {
         y0 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j));
         y1 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j + 1));
       }
@@ -1439,7 +1492,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     if (l + 1 < L)
       gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);
-    else if (FMT == 1 && p.lm_fmt == 0)  // int8 projections, bf16 lm_head
+    else if (FMT != 0 && p.lm_fmt == 0)  // quantized projections, bf16 lm_head
       gemv_prefetch<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
     else
       gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
@@ -1447,7 +1500,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     stamp();
   }
   // final RMSNorm -> lm_head (in the lm_head's own storage format, which sets the LDS layout)
-  const bool head16 = FMT == 1 && p.lm_fmt == 0;
+  const bool head16 = FMT != 0 && p.lm_fmt == 0;
   if (head16) ok = norm_from_x<0>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
   else ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
   stamp();
@@ -1477,19 +1530,27 @@ template __global__ void amk_decode_kernel<64, 0, 8>(const KParams);
 template __global__ void amk_decode_kernel<64, 1, 8>(const KParams);
 template __global__ void amk_decode_kernel<128, 0, 8>(const KParams);
 template __global__ void amk_decode_kernel<128, 1, 8>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 4>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 4>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 8>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 8>(const KParams);
 
 }  // namespace amk
 
 // host-visible handles of the kernel instantiations (defined in this translation unit)
+// fmt: 0 bf16, 1 int8, 2 int4 projection weights
 extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax) {
   using namespace amk;
-  if (gmax == 4) {
-    if (head_dim == 64) return fmt ? (const void*)&amk_decode_kernel<64, 1, 4> : (const void*)&amk_decode_kernel<64, 0, 4>;
-    if (head_dim == 128) return fmt ? (const void*)&amk_decode_kernel<128, 1, 4> : (const void*)&amk_decode_kernel<128, 0, 4>;
-  } else if (gmax == 8) {
-    if (head_dim == 64) return fmt ? (const void*)&amk_decode_kernel<64, 1, 8> : (const void*)&amk_decode_kernel<64, 0, 8>;
-    if (head_dim == 128) return fmt ? (const void*)&amk_decode_kernel<128, 1, 8> : (const void*)&amk_decode_kernel<128, 0, 8>;
-  }
-  return nullptr;
+  const void* const t[2][2][3] = {
+      {{(const void*)&amk_decode_kernel<64, 0, 4>, (const void*)&amk_decode_kernel<64, 1, 4>,
+        (const void*)&amk_decode_kernel<64, 2, 4>},
+       {(const void*)&amk_decode_kernel<64, 0, 8>, (const void*)&amk_decode_kernel<64, 1, 8>,
+        (const void*)&amk_decode_kernel<64, 2, 8>}},
+      {{(const void*)&amk_decode_kernel<128, 0, 4>, (const void*)&amk_decode_kernel<128, 1, 4>,
+        (const void*)&amk_decode_kernel<128, 2, 4>},
+       {(const void*)&amk_decode_kernel<128, 0, 8>, (const void*)&amk_decode_kernel<128, 1, 8>,
+        (const void*)&amk_decode_kernel<128, 2, 8>}}};
+  if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 2) return nullptr;
+  return t[head_dim == 128][gmax == 8][fmt];
 }
 extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle() { return (const void*)&amk::amk_barrier_kernel; }

@@ -47,7 +47,9 @@ inline float bf16_to_float(uint16_t b) {
 
 // Quantizes rows [r0, r1) of a bf16 matrix: s = amax / 127 (IEEE fp32 division), q =
 // clamp(nearbyint(w / s), -127, 127) with the default round-to-nearest-even mode.
-void quantize_rows(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8_t* codes, float* scales) {
+// Symmetric per-row quantizer with codes in [-qmax, qmax] (127: int8, 7: int4).
+void quantize_rows(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8_t* codes, float* scales,
+                   float qmax) {
   for (int64_t r = r0; r < r1; ++r) {
     const uint16_t* row = w + r * cols;
     float amax = 0.f;
@@ -58,12 +60,12 @@ void quantize_rows(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8
       std::memset(out, 0, static_cast<size_t>(cols));
       continue;
     }
-    volatile float denom = 127.0f;  // keep a true division (never a reciprocal multiply)
+    volatile float denom = qmax;  // keep a true division (never a reciprocal multiply)
     const float s = amax / denom;
     scales[r] = s;
     for (int64_t c = 0; c < cols; ++c) {
       float q = std::nearbyint(bf16_to_float(row[c]) / s);
-      q = std::min(127.0f, std::max(-127.0f, q));
+      q = std::min(qmax, std::max(-qmax, q));
       out[c] = static_cast<int8_t>(q);
     }
   }
@@ -126,8 +128,11 @@ int validate_config(const amk_config* c) {
   if (c->hidden > 8192) return fail(AMK_ERR_UNSUPPORTED, "hidden > 8192");
   if (c->ffn > 32768 || c->n_q_heads * c->head_dim > 32768) return fail(AMK_ERR_UNSUPPORTED, "ffn or q dim > 32768");
   if (c->vocab % 2) return fail(AMK_ERR_UNSUPPORTED, "vocab must be even");
-  if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16 && c->weight_format != AMK_W8A16_BF16_HEAD)
+  if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16 && c->weight_format != AMK_W8A16_BF16_HEAD &&
+      c->weight_format != AMK_W4A16)
     return fail(AMK_ERR_UNSUPPORTED, "weight_format");
+  if (c->weight_format == AMK_W4A16 && (c->hidden % 32 || c->ffn % 32 || (c->n_q_heads * c->head_dim) % 32))
+    return fail(AMK_ERR_UNSUPPORTED, "W4A16 needs hidden, ffn and n_q_heads*head_dim multiples of 32");
   if (c->rope_scale_factor > 1.0f &&
       !(c->rope_low_freq_factor > 0.0f && c->rope_high_freq_factor > c->rope_low_freq_factor &&
         c->rope_original_ctx > 0))
@@ -182,7 +187,14 @@ const char* amk_status_string(int status) {
 int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes, float* scales) {
   if (!w || !codes || !scales) return fail(AMK_ERR_INVALID_ARG, "null pointer");
   if (rows <= 0 || cols <= 0) return fail(AMK_ERR_INVALID_ARG, "non-positive size");
-  parallel_rows(rows, [&](int64_t a, int64_t b) { quantize_rows(w, cols, a, b, codes, scales); });
+  parallel_rows(rows, [&](int64_t a, int64_t b) { quantize_rows(w, cols, a, b, codes, scales, 127.0f); });
+  return AMK_OK;
+}
+
+int amk_quantize_int4(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes, float* scales) {
+  if (!w || !codes || !scales) return fail(AMK_ERR_INVALID_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0) return fail(AMK_ERR_INVALID_ARG, "non-positive size");
+  parallel_rows(rows, [&](int64_t a, int64_t b) { quantize_rows(w, cols, a, b, codes, scales, 7.0f); });
   return AMK_OK;
 }
 
@@ -201,9 +213,10 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
   const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd;
   const int64_t QKV = QD + 2 * KD;
-  const bool q8 = c.weight_format != AMK_BF16;         // int8 projections
+  const bool q8 = c.weight_format != AMK_BF16;         // quantized projections (int8 or int4)
   const bool lm_q8 = c.weight_format == AMK_W8A16;     // int8 lm_head
-  const int64_t wb = q8 ? 1 : 2;
+  const int pbits = c.weight_format == AMK_BF16 ? 16 : (c.weight_format == AMK_W4A16 ? 4 : 8);  // projections
+  const int kfmt = pbits == 16 ? 0 : (pbits == 8 ? 1 : 2);  // kernel weight format
 
   auto m = new amk_model();
   m->cfg = c;
@@ -219,8 +232,8 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   // ---------------- layout ----------------
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  const size_t l_qkv = static_cast<size_t>(QKV * H * wb), l_o = static_cast<size_t>(H * QD * wb);
-  const size_t l_gu = static_cast<size_t>(2 * F * H * wb), l_d = static_cast<size_t>(H * F * wb);
+  const size_t l_qkv = static_cast<size_t>(QKV * H * pbits / 8), l_o = static_cast<size_t>(H * QD * pbits / 8);
+  const size_t l_gu = static_cast<size_t>(2 * F * H * pbits / 8), l_d = static_cast<size_t>(H * F * pbits / 8);
   const size_t off_embed = take(static_cast<size_t>(V * H * 2));
   m->off_qkv = take(l_qkv * L);
   m->off_o = take(l_o * L);
@@ -246,13 +259,13 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   m->gmax = G <= 4 ? 4 : 8;
   {
     const char* kv = std::getenv("AMK_KERNEL");
-    m->stream = kv && std::string(kv) == "block" && c.weight_format != AMK_W8A16_BF16_HEAD;
+    m->stream = kv && std::string(kv) == "block" && (c.weight_format == AMK_BF16 || c.weight_format == AMK_W8A16);
   }
   if (m->stream && m->gmax != 4) m->stream = false;  // the block-split kernel covers G <= 4
   // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
   // of one output on the lanes of a wave, so it takes at most 64
   m->s_cap = std::min(64, std::max(1, m->grid / c.n_kv_heads));
-  const int cw = q8 ? 1024 : 512;
+  const int cw = 8192 / pbits;  // columns per 1 KB weight chunk
   auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
   auto a4 = [](int64_t n) { return (n + 3) / 4 * 4; };
   const int64_t xs_f = std::max({pad(H), pad(QD), pad(F)});
@@ -283,7 +296,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     const int64_t rows = static_cast<int64_t>(amk::kWaves) * (512 / hd);
     const int64_t attn_f = rows * m->gmax * (hd + 4) + 4 * m->gmax + G * hd + hd;
     m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
-    m->kernel = amk_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
+    m->kernel = amk_kernel_handle(static_cast<int>(hd), kfmt, m->gmax);
   }
   if (m->lds_bytes > 160 * 1024) { delete m; return fail(AMK_ERR_UNSUPPORTED, "LDS need exceeds 160 KB"); }
   if (!m->kernel) { delete m; return fail(AMK_ERR_UNSUPPORTED, "no kernel variant"); }
@@ -328,10 +341,12 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     return AMK_OK;
   };
   // Packs rows of one layer's matrix given a row map (packed row -> source pointer).
-  auto pack_matrix = [&](bool quant, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
+  // bits: 16 (bf16 rows copied), 8 (int8 codes) or 4 (int4 codes, column c of a row in byte c / 2,
+  // the low nibble for even c, two's complement)
+  auto pack_matrix = [&](int bits, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
                          const std::vector<const uint16_t*>& src_tensors,
                          auto&& row_source) -> int {
-    if (quant) {
+    if (bits != 16) {
       // quantize each source tensor in canonical order, then permute rows
       std::vector<std::vector<int8_t>> qc(src_tensors.size());
       std::vector<std::vector<float>> qs(src_tensors.size());
@@ -340,7 +355,8 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
         for (int64_t r = 0; r < rows; ++r) { int w; int64_t sr; row_source(r, &w, &sr); if (w == static_cast<int>(k)) ++r_k; }
         qc[k].resize(static_cast<size_t>(r_k * cols));
         qs[k].resize(static_cast<size_t>(r_k));
-        int e = amk_quantize_int8(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data());
+        int e = bits == 8 ? amk_quantize_int8(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data())
+                          : amk_quantize_int4(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data());
         if (e) return e;
       }
       codes.resize(static_cast<size_t>(rows * cols));
@@ -350,7 +366,14 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
         std::memcpy(codes.data() + r * cols, qc[w].data() + sr * cols, static_cast<size_t>(cols));
         scales[static_cast<size_t>(r)] = qs[w][static_cast<size_t>(sr)];
       }
-      int e = upload(dst_w, codes.data(), static_cast<size_t>(rows * cols));
+      if (bits == 4) {  // two codes per byte, in place (byte i is written after codes 2i, 2i + 1 are read)
+        const int64_t n = rows * cols / 2;
+        for (int64_t i = 0; i < n; ++i)
+          codes[static_cast<size_t>(i)] = static_cast<int8_t>(
+              (static_cast<uint8_t>(codes[static_cast<size_t>(2 * i)]) & 0x0F) |
+              ((static_cast<uint8_t>(codes[static_cast<size_t>(2 * i + 1)]) & 0x0F) << 4));
+      }
+      int e = upload(dst_w, codes.data(), static_cast<size_t>(rows * cols * bits / 8));
       if (e) return e;
       return upload(dst_s, scales.data(), static_cast<size_t>(rows) * 4);
     }
@@ -370,23 +393,23 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
       nin[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[0][i]);
       npost[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[5][i]);
     }
-    rc = pack_matrix(q8, QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
+    rc = pack_matrix(pbits, QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
                      [&](int64_t r, int* w, int64_t* sr) { qkv_source(c, r, w, sr); });
     if (rc) break;
-    rc = pack_matrix(q8, H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
+    rc = pack_matrix(pbits, H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
     if (rc) break;
-    rc = pack_matrix(q8, 2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
+    rc = pack_matrix(pbits, 2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = static_cast<int>(r & 1); *sr = r >> 1; });
     if (rc) break;
-    rc = pack_matrix(q8, H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
+    rc = pack_matrix(pbits, H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) {
     for (int64_t i = 0; i < H; ++i) nfin[static_cast<size_t>(i)] = bf16_to_float(t[1 + 9 * L][i]);
     const uint16_t* lm = c.tied_embeddings ? t[0] : t[2 + 9 * L];
     if (!lm_shares_embed)
-      rc = pack_matrix(lm_q8, V, H, m->off_lm, m->off_slm, {lm},
+      rc = pack_matrix(lm_q8 ? 8 : 16, V, H, m->off_lm, m->off_slm, {lm},
                        [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) rc = upload(off_nin, nin.data(), nin.size() * 4);
@@ -564,10 +587,12 @@ int amk_get_info(const amk_model* m, amk_info* info) {
 int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, float* scales_out) {
   if (!m || !codes_out || !scales_out) return fail(AMK_ERR_INVALID_ARG, "null pointer");
   const amk_config& c = m->cfg;
-  if (c.weight_format == AMK_BF16) return fail(AMK_ERR_UNSUPPORTED, "model is not W8A16");
+  if (c.weight_format == AMK_BF16) return fail(AMK_ERR_UNSUPPORTED, "model has no quantized weights");
   const int L = c.n_layers;
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
   const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd, QKV = QD + 2 * KD;
+  const int pbits = c.weight_format == AMK_W4A16 ? 4 : 8;  // projection code width
+  auto lb = [&](int64_t n) { return static_cast<size_t>(n * pbits / 8); };  // bytes of n codes
   const int lm_idx = c.tied_embeddings ? 0 : 2 + 9 * L;
   int64_t rows = 0, cols = 0, mrows = 0;
   size_t wsrc = 0, ssrc = 0;
@@ -581,20 +606,27 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
     switch (o) {
       case 1: case 2: case 3:
         kind = 0; which = o - 1; rows = (o == 1) ? QD : KD; cols = H; mrows = QKV;
-        wsrc = m->off_qkv + static_cast<size_t>(l) * QKV * H; ssrc = m->off_sqkv + 4 * static_cast<size_t>(QKV) * l; break;
-      case 4: kind = 1; rows = mrows = H; cols = QD; wsrc = m->off_o + static_cast<size_t>(l) * H * QD; ssrc = m->off_so + 4 * static_cast<size_t>(H) * l; break;
+        wsrc = m->off_qkv + l * lb(QKV * H); ssrc = m->off_sqkv + 4 * static_cast<size_t>(QKV) * l; break;
+      case 4: kind = 1; rows = mrows = H; cols = QD; wsrc = m->off_o + l * lb(H * QD); ssrc = m->off_so + 4 * static_cast<size_t>(H) * l; break;
       case 6: case 7:
         kind = 2; which = o - 6; rows = F; cols = H; mrows = 2 * F;
-        wsrc = m->off_gu + static_cast<size_t>(l) * 2 * F * H; ssrc = m->off_sgu + 4 * static_cast<size_t>(2 * F) * l; break;
-      case 8: kind = 3; rows = mrows = H; cols = F; wsrc = m->off_d + static_cast<size_t>(l) * H * F; ssrc = m->off_sd + 4 * static_cast<size_t>(H) * l; break;
+        wsrc = m->off_gu + l * lb(2 * F * H); ssrc = m->off_sgu + 4 * static_cast<size_t>(2 * F) * l; break;
+      case 8: kind = 3; rows = mrows = H; cols = F; wsrc = m->off_d + l * lb(H * F); ssrc = m->off_sd + 4 * static_cast<size_t>(H) * l; break;
       default: break;
     }
   }
   if (kind < 0) return fail(AMK_ERR_INVALID_ARG, "tensor index is not a quantized matrix");
+  const int bits = kind == 4 ? 8 : pbits;
   std::vector<int8_t> allc(static_cast<size_t>(mrows * cols));
   std::vector<float> alls(static_cast<size_t>(mrows));
-  HIP_TRY(hipMemcpy(allc.data(), m->weights + wsrc, allc.size(), hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(allc.data(), m->weights + wsrc, static_cast<size_t>(mrows * cols * bits / 8), hipMemcpyDeviceToHost));
   HIP_TRY(hipMemcpy(alls.data(), m->weights + ssrc, alls.size() * 4, hipMemcpyDeviceToHost));
+  if (bits == 4)  // unpack in place from the back: byte i holds codes 2i (low nibble) and 2i + 1
+    for (int64_t i = mrows * cols / 2 - 1; i >= 0; --i) {
+      const uint8_t b = static_cast<uint8_t>(allc[static_cast<size_t>(i)]);
+      allc[static_cast<size_t>(2 * i + 1)] = static_cast<int8_t>(static_cast<int8_t>(b & 0xF0) >> 4);
+      allc[static_cast<size_t>(2 * i)] = static_cast<int8_t>(static_cast<int8_t>(b << 4) >> 4);
+    }
   for (int64_t r = 0; r < mrows; ++r) {
     int w = 0;
     int64_t sr = r;

@@ -44,6 +44,8 @@ extern "C" {
 #define AMK_W8A16 1 /* weights int8, one fp32 scale per output row; activations bf16      */
 #define AMK_W8A16_BF16_HEAD 2 /* AMK_W8A16 projections, lm_head kept bf16 (for a tied model the
                                  head reads the bf16 embedding table; no quantized copy)      */
+#define AMK_W4A16 3 /* projections int4 (two codes per byte), one fp32 scale per output row;
+                       lm_head kept bf16 as in AMK_W8A16_BF16_HEAD; activations bf16           */
 
 /* Model description. Weights follow HuggingFace LlamaForCausalLM: pre-norm RMSNorm,
  * rotate-half RoPE with inv_freq_i = rope_theta^(-2i/head_dim), grouped-query attention
@@ -62,7 +64,7 @@ typedef struct {
   float rms_eps;           /* RMSNorm epsilon                                                */
   float rope_theta;        /* RoPE base                                                      */
   int32_t tied_embeddings; /* 1: lm_head is embed_tokens                                     */
-  int32_t weight_format;   /* AMK_BF16, AMK_W8A16 or AMK_W8A16_BF16_HEAD                     */
+  int32_t weight_format;   /* AMK_BF16, AMK_W8A16, AMK_W8A16_BF16_HEAD or AMK_W4A16          */
   /* Llama-3 RoPE frequency scaling (the rule Llama 3.1 / 3.2 checkpoints declare; the pages do
    * not describe it): rope_scale_factor <= 1 means none. Otherwise a frequency f with
    * wavelength 2 pi / f shorter than rope_original_ctx / rope_high_freq_factor is kept, one
@@ -116,11 +118,17 @@ typedef struct {
  * int8-weights reading in which only the projections shrink: the pages quote int8 weight bytes
  * at 0.61 of bf16, a figure a bf16 head explains; gist.science explainer, Experimental
  * Results).
+ * AMK_W4A16 quantizes the projections with amk_quantize_int4 and keeps the lm_head bf16 (the
+ * pages' int4 weight-only variant: lossy, 2.42x less weight traffic than bf16; gist.science
+ * explainer, Technical Summary > Key Contributions; this format streams 1/2.44 of the bf16
+ * weight bytes of a SmolLM2-135M or Llama-3.2-1B shape). Device row layout: code of column c
+ * in byte c / 2, low nibble for even c, two's complement.
  * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
  * *out receives a model handle owned by the library until amk_free.
  * Errors: INVALID_ARG (null pointers, wrong n_tensors), UNSUPPORTED (shape checks: head_dim
- * in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd multiples of 16, vocab
- * and hidden even, max_ctx >= 1), HIP, OOM, COOPERATIVE (no co-resident persistent grid). */
+ * in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd multiples of 16, or of 32
+ * for AMK_W4A16, vocab and hidden even, max_ctx >= 1), HIP, OOM, COOPERATIVE (no co-resident
+ * persistent grid). */
 int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_tensors,
                      int32_t n_tensors, amk_model** out);
 
@@ -168,12 +176,12 @@ size_t amk_kv_cache_bytes(const amk_model* m);
 /* Launch geometry and sizes of a loaded model. */
 int amk_get_info(const amk_model* m, amk_info* info);
 
-/* Copies the int8 codes and fp32 row scales the library uses for canonical tensor
- * `tensor_index` (a W8A16 projection, or, for AMK_W8A16, the lm_head index 2+9L / embed index 0
- * for a tied model) back to host memory in canonical [rows][cols] order. codes_out: host int8
- * [rows*cols]; scales_out: host fp32 [rows]. Errors: INVALID_ARG for a tensor that is not
- * quantized (including the bf16 head of AMK_W8A16_BF16_HEAD); UNSUPPORTED for an AMK_BF16
- * model. */
+/* Copies the codes and fp32 row scales the library uses for canonical tensor `tensor_index`
+ * (a quantized projection, or, for AMK_W8A16, the lm_head index 2+9L / embed index 0 for a
+ * tied model) back to host memory in canonical [rows][cols] order, one code per int8 (int4
+ * codes unpacked, in [-7, 7]). codes_out: host int8 [rows*cols]; scales_out: host fp32 [rows].
+ * Errors: INVALID_ARG for a tensor that is not quantized (including the bf16 head of
+ * AMK_W8A16_BF16_HEAD and AMK_W4A16); UNSUPPORTED for an AMK_BF16 model. */
 int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes_out,
                          float* scales_out);
 
@@ -186,6 +194,16 @@ int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes
  * [rows][cols]; scales: host fp32 [rows]. Errors: INVALID_ARG for null pointers or
  * non-positive sizes. */
 int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
+                      float* scales);
+
+/* Host quantizer of AMK_W4A16 (no GPU needed): the same rule at four bits. For row n: amax =
+ * max |w|, s = fp32(amax / 7) by IEEE division, q = clamp(round half to even(fp32(w / s)), -7,
+ * 7); an all-zero row gives s = 0 and q = 0. The pages name int4 weight-only quantization as
+ * lossy with 2.42x less weight traffic (gist.science explainer, Technical Summary > Key
+ * Contributions) without its format; this per-row rule is the W8A16 one at four bits.
+ * w: host bf16 bit patterns [rows][cols]; codes: host int8 [rows][cols], one code per byte;
+ * scales: host fp32 [rows]. Errors: INVALID_ARG for null pointers or non-positive sizes. */
+int amk_quantize_int4(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
                       float* scales);
 
 /* Measures a classic grid barrier (arrival counters + polling, the pattern the tagged hand-offs

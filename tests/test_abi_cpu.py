@@ -12,7 +12,7 @@ import torch
 
 import decode_megakernel_cooperative_amd as D
 from decode_megakernel_cooperative_amd import amk as A
-from oracle.quant import quantize_rows_int8
+from oracle.quant import quantize_rows_int4, quantize_rows_int8
 import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -45,6 +45,23 @@ def test_host_quantizer_worked_rows():
     d = json.load(open(os.path.join(ROOT, "tests", "golden", "quant_tie_row.json")))
     for row in d["rows"]:
         c, s = D.amk_quantize_int8(_bits(np.array([row["w_float"]], np.float32)))
+        assert c[0].tolist() == row["codes"], row["why"]
+        assert s[0] == np.float32(row["scale"])
+
+
+@pytest.mark.parametrize("rows,cols,std", [(96, 576, 0.02), (33, 4096, 0.02), (7, 1536, 0.5), (64, 2048, 3.0)])
+def test_host_int4_quantizer_bit_exact_vs_oracle(rows, cols, std):
+    w = _bits(np.random.default_rng(rows * cols + 4).standard_normal((rows, cols)) * std)
+    c1, s1 = D.amk_quantize_int4(w)
+    c2, s2 = quantize_rows_int4(w)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_host_int4_quantizer_worked_rows():
+    d = json.load(open(os.path.join(ROOT, "tests", "golden", "quant4_tie_row.json")))
+    for row in d["rows"]:
+        c, s = D.amk_quantize_int4(_bits(np.array([row["w_float"]], np.float32)))
         assert c[0].tolist() == row["codes"], row["why"]
         assert s[0] == np.float32(row["scale"])
 
@@ -92,6 +109,11 @@ def test_argument_validation_without_gpu():
     fs = ctypes.c_float()
     assert lib.amk_bench_barrier(0, ctypes.byref(fs)) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_quantize_int8(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_quantize_int4(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
+    # W4A16 rows must hold whole 16-byte lane loads: 32-column multiples
+    bad = D.make_config(W.SMOLLM2_135M, 32, D.AMK_W4A16)
+    bad.ffn = 1552
+    assert lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h)) == A.AMK_ERR_UNSUPPORTED
     assert "invalid argument" in D.amk_status_string(A.AMK_ERR_INVALID_ARG)
 
 

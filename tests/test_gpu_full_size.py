@@ -69,3 +69,7 @@ def test_llama3_8b_bf16_ctx4096():
 
 def test_llama3_8b_w8a16_ctx32768():
     _run("llama3-8b-w8a16-ctx32768", steps=2, conditioned_steps=1)
+
+
+def test_llama3_8b_w4a16_ctx4096():
+    _run("llama3-8b-w4a16-ctx4096", steps=2, conditioned_steps=1)

@@ -10,7 +10,7 @@ import torch
 
 import decode_megakernel_cooperative_amd as D
 import workloads as W
-from oracle.quant import quantize_rows_int8
+from oracle.quant import quantize_rows_int4, quantize_rows_int8
 from gpu_harness import LOGIT_TOL, build, log, run_teacher_forced
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +132,38 @@ def test_w8a16_with_bf16_head(which):
     toks = W.gen_tokens(shape, 8, seed0=12)
     res = run_teacher_forced(dec, orc, kv, shape, pre, toks[:4], 12)
     _assert_gates(res, f"w8a16 bf16 head {which}")
+    dec.close()
+
+
+@pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied"])
+def test_w4a16_parity(which):
+    """Int4 per-row projections (two codes per byte) with the lm_head kept bf16: every
+    projection's codes and scales bit-exact against the oracle's quantizer, then the logit and
+    greedy gates over prompt and greedy steps (multi-split attention for the prefilled shape)."""
+    if which == "smollm2-tied":
+        shape, ctx, pre, n_prompt, n_greedy = W.SMOLLM2_135M, 48, 0, 16, 24
+    else:
+        shape, ctx, pre, n_prompt, n_greedy = (W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False,
+                                                            500000.0), 340, 300, 4, 12)
+    dec, orc, kv = build(shape, W.FMT_W4A16, ctx, pre, seed0=13)
+    ws = W.gen_weights(shape, 13)
+    checked = 0
+    for i, (name, dims, kind) in enumerate(W.tensor_specs(shape)):
+        if kind != "matrix" or i == 0 or (not shape.tied and i == 2 + 9 * shape.n_layers):
+            continue
+        codes, scales = D.amk_export_quantized(dec.model, i, dims[0], dims[1])
+        c_ref, s_ref = quantize_rows_int4(W.bf16_bits(ws[i]))
+        assert np.array_equal(codes, c_ref), name
+        assert np.array_equal(scales.view(np.uint32), s_ref.view(np.uint32)), name
+        checked += 1
+    assert checked == 7 * shape.n_layers
+    lm_idx = 0 if shape.tied else 2 + 9 * shape.n_layers
+    with pytest.raises(D.AmkError):
+        D.amk_export_quantized(dec.model, lm_idx, shape.vocab, shape.hidden)
+    del ws
+    toks = W.gen_tokens(shape, n_prompt, seed0=13)
+    res = run_teacher_forced(dec, orc, kv, shape, pre, toks, n_greedy, check_kv=True)
+    _assert_gates(res, f"w4a16 {which}")
     dec.close()
 
 
