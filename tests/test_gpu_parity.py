@@ -96,6 +96,26 @@ def test_long_split_current_position_late_in_unit(fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("which", ["hd128", "hd64"])
+def test_single_split_boundary(which):
+    """A context that one block covers in a single pipeline step (8 waves x 4 groups x 512 /
+    head_dim positions: 128 at head_dim 128, 256 at head_dim 64) runs one split per kv head,
+    which writes the attention output without the split merge; one position more switches to
+    many splits. Steps on both sides of the switch, and the current position at the last slot of
+    the single split."""
+    if which == "hd128":
+        shape, tstep = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0), 128
+    else:
+        shape, tstep = W.ModelShape("hd64-gqa3", 576, 3, 9, 3, 64, 1536, 1000, True, 10000.0), 256
+    pre = tstep - 2
+    dec, orc, kv = build(shape, D.AMK_W8A16, tstep + 3, pre, seed0=11)
+    tok = W.gen_tokens(shape, 1, seed0=11)[0]
+    # positions tstep-2, tstep-1 (contexts tstep-1, tstep: one split), tstep, tstep+1 (many)
+    res = run_teacher_forced(dec, orc, kv, shape, pre, [], 4, first_token=tok, check_kv=True)
+    _assert_gates(res, f"single-split boundary {which}")
+    dec.close()
+
+
 @pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
 def test_block_split_kernel_parity(fmt, monkeypatch):
     """The alternative block-split kernel (AMK_KERNEL=block at load time) against the oracle on
