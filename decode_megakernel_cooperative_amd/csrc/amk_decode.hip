@@ -724,8 +724,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   A = 1.f;
   B = 0.f;
   if (k < g.pb) {
-    if (FMT == 1) A = Sc[row];
-    if (FMT == 2) A = Sc[row] * 16.f;  // exact: the int4 products arrive as q / 16
+    if (FMT != 0) A = Sc[row];  // int4: the epilogue applies the factor 16
     if (EPI == EPI_RESID) {
       B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
                            : ld_payload(p.tx + row);
@@ -847,6 +846,10 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       if (FMT != 0) {
         y0 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j));
         y1 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j + 1));
+      }
+      if (FMT == 2) {  // the int4 products arrived as q / 16 (exact)
+        y0 *= 16.f;
+        y1 *= 16.f;
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
