@@ -1228,18 +1228,25 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       A0 += dpp<0x4E>(A0);
       A1 += dpp<0x4E>(A1);
     }
-    if (sub != 0) continue;
+    // every lane of the quad holds both sums now
     const float M = hs[2 * h], Ls = hs[2 * h + 1];
     if (S == 1) {
+      if (sub != 0) continue;
       const float inv = 1.0f / Ls;
       st_tag(p.to + ((g * G + h) * HD + d) / 2,
              static_cast<uint32_t>(f32_to_bf16(A0 * inv)) | (static_cast<uint32_t>(f32_to_bf16(A1 * inv)) << 16),
              to_tag);
     } else {
+      // lanes 0 and 1 of the quad store the pair's two words with one store instruction, so a
+      // wave writes whole runs of consecutive words (whole cache sectors)
       uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
-      st_tag(dst + d, __float_as_uint(A0), tpart);
-      st_tag(dst + d + 1, __float_as_uint(A1), tpart);
-      if (d == 0) {
+      if (NS >= 2) {
+        if (sub < 2) st_tag(dst + d + sub, __float_as_uint(sub == 0 ? A0 : A1), tpart);
+      } else {
+        st_tag(dst + d, __float_as_uint(A0), tpart);
+        st_tag(dst + d + 1, __float_as_uint(A1), tpart);
+      }
+      if (d == 0 && sub == 0) {
         st_tag(dst + HD, __float_as_uint(M), tpart);
         st_tag(dst + HD + 1, __float_as_uint(Ls), tpart);
       }
