@@ -48,7 +48,7 @@ def test_greedy_token_is_argmax_of_its_logits():
     dec.close()
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W8A16_BF16_HEAD, D.AMK_W4A16])
 def test_greedy_ties_go_to_lowest_index(fmt):
     """An lm_head whose rows repeat two row patterns (+r and -r) gives logits with only two
     distinct values, each shared by hundreds of indices spread over all blocks: the token must be
@@ -85,6 +85,27 @@ def _chain(dec, tok0, pos0, n, stream=None):
     for i in range(n):
         dec.step_greedy(toks[i:i + 1], pos0 + i, next_token_out=toks[i + 1:i + 2], logits_out=lgs[i], stream=stream)
     return toks, lgs
+
+
+def test_greedy_w4a16_chain_follows_the_oracle():
+    """A device chain on the W4A16 format (int4 projections, bf16 lm_head): every written token
+    is the argmax of its own logits, and the chain is valid against the oracle replaying it."""
+    dec, orc, kv = build(SHAPE, D.AMK_W4A16, 40, 16, seed0=8)
+    tok0 = W.gen_tokens(SHAPE, 1, seed0=8)[0]
+    toks, lgs = _chain(dec, tok0, 16, 12)
+    torch.cuda.synchronize()
+    dec.sync()
+    toks, lgs = toks.cpu().numpy(), lgs.cpu().numpy()
+    checked = 0
+    for i in range(12):
+        assert int(toks[i + 1]) == int(np.argmax(lgs[i])), i
+        o = orc.decode_step(int(toks[i]), 16 + i, kv)
+        assert float(np.max(np.abs(lgs[i] - o))) <= LOGIT_TOL, i
+        if top2_margin(o) > MARGIN:
+            assert int(toks[i + 1]) == int(np.argmax(o)), i
+            checked += 1
+    log(f"  w4a16 chain: {checked} of 12 steps above the margin")
+    dec.close()
 
 
 def test_greedy_chain_follows_the_oracle():
