@@ -355,9 +355,10 @@ __device__ __forceinline__ int toff(const KParams& p, const uint64_t* buf) {
   return static_cast<int>(reinterpret_cast<const uint8_t*>(buf) - reinterpret_cast<const uint8_t*>(p.tagged));
 }
 
-// Bound of a hand-off wait, checked after its round `it`: false once the step must be abandoned.
-// The error word is read every 16 rounds (an error raised elsewhere keeps its code); the clock
-// also at round 2, so that a spin limit of one tick ends the first poll that waits at all.
+// Bound of a hand-off wait, checked after its reload number `it`: false once the step must be
+// abandoned. The error word is read every 16 reloads (an error raised elsewhere keeps its code);
+// the clock also after the second reload, so that a spin limit of one tick ends the first poll
+// that waits at all.
 __device__ __forceinline__ bool wait_ok(const KParams& p, unsigned it, uint64_t t_start) {
   const bool round16 = (it & 15u) == 0;
   if (round16 && ldc(p.err) != 0u) return false;

@@ -27,7 +27,7 @@ struct KParams {
   int32_t* next_token;                      // greedy step: argmax of the logits (else null)
   // packed weights: per layer, rows are stored in the order the kernel consumes them
   const uint8_t* w_qkv; int64_t w_qkv_ls;   // bytes per layer
-  const float* s_qkv;   int64_t s_qkv_ls;   // fp32 scales per layer (W8A16 only)
+  const float* s_qkv;   int64_t s_qkv_ls;   // fp32 row scales per layer (int8 / int4 weights only)
   const uint8_t* w_o;   int64_t w_o_ls;
   const float* s_o;     int64_t s_o_ls;
   const uint8_t* w_gu;  int64_t w_gu_ls;
@@ -56,7 +56,7 @@ struct KParams {
   uint64_t* tx;                             // [H] residual (fp32)
   uint64_t* tq;                             // [nq*hd] rotated queries (fp32)
   uint64_t* tkv;                            // [2][nkv][hd/2] K/V of pos, bf16 dims (i, i+hd/2)
-  uint64_t* tpart;                          // [nq][s_cap][hd+2] split partials: values, max, sum
+  uint64_t* tpart;                          // [nq][s_cap][hd+2] split partials: values, max (base 2), sum
   uint64_t* to;                             // [nq*hd/2] attention output, 2 bf16 per word
   uint64_t* targ;                           // [grid][2] greedy step: each block's argmax (value, index)
   uint64_t* tm;                             // SwiGLU output: [F] 32-bit words bf16 << 16 | tag & 0xffff
