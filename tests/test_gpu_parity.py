@@ -96,6 +96,28 @@ def test_long_split_current_position_late_in_unit(fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16])
+@pytest.mark.parametrize("which", ["hd128-g8", "hd64-g6"])
+def test_large_query_groups(which, fmt):
+    """More than 4 query heads per kv head (the kernel variant that holds 8 heads per K/V load):
+    prompt steps from an empty cache (one split per kv head), then steps on a prefilled cache
+    with many splits."""
+    if which == "hd128-g8":
+        shape = W.ModelShape("hd128-g8", 512, 2, 16, 2, 128, 1024, 1000, False, 500000.0)
+    else:
+        shape = W.ModelShape("hd64-g6", 384, 2, 12, 2, 64, 1024, 2000, True, 10000.0)
+    dec, orc, kv = build(shape, fmt, 16, 0, seed0=4)
+    toks = W.gen_tokens(shape, 6, seed0=4)
+    res = run_teacher_forced(dec, orc, kv, shape, 0, toks, 4, check_kv=True)
+    _assert_gates(res, f"{which} fmt{fmt} fresh")
+    dec.close()
+    dec, orc, kv = build(shape, fmt, 420, 400, seed0=6)
+    tok = W.gen_tokens(shape, 1, seed0=6)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 400, [], 6, first_token=tok, check_kv=True)
+    _assert_gates(res, f"{which} fmt{fmt} prefilled")
+    dec.close()
+
+
 @pytest.mark.parametrize("which", ["hd128", "hd64"])
 def test_single_split_boundary(which):
     """A context that one block covers in a single pipeline step (8 waves x 4 groups x 512 /
