@@ -932,6 +932,11 @@ struct AttnRegs {
   i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
 };
 
+// Running maxima start at a finite floor below every score, so the softmax weights need no
+// special case: exp2(-inf - m) and exp2(floor - m) are both 0 for any score m, and a row that has
+// seen no position keeps weight 0.
+constexpr float kScoreFloor = -1.0e30f;
+
 // LDS of the attention stage, in floats: every row's softmax state (a row is the LPP lanes that
 // hold one position of a wave load: [R][GMAX][RS] = values, running max, running sum, merge
 // weight, pad), then each head's block max and sum, then q of the G heads and K/V(pos).
@@ -1073,7 +1078,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     float mr[GMAX], lr[GMAX], acc[GMAX][8];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
-      mr[h] = NEG_INF;
+      mr[h] = kScoreFloor;
       lr[h] = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
@@ -1114,13 +1119,13 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         float mnew = mr[h];
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) mnew = fmaxf(mnew, s[uu][h]);
-        const float corr = (mr[h] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mr[h] - mnew);
+        const float corr = __builtin_amdgcn_exp2f(mr[h] - mnew);
         lr[h] *= corr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
 #pragma unroll
         for (int uu = 0; uu < kAttnU; ++uu) {
-          pe[uu][h] = (s[uu][h] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(s[uu][h] - mnew);
+          pe[uu][h] = __builtin_amdgcn_exp2f(s[uu][h] - mnew);
           lr[h] += pe[uu][h];
         }
         mr[h] = mnew;
