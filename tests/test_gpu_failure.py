@@ -50,7 +50,7 @@ def test_forced_timeout_is_reported_and_recovered():
     dec.close()
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16])
 def test_last_cache_slot(fmt):
     """A step at pos = max_ctx - 1 (the cache's last slot) on a prefilled cache."""
     shape = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0)

@@ -152,6 +152,20 @@ def test_block_split_kernel_parity(fmt, monkeypatch):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_W8A16_BF16_HEAD, D.AMK_W4A16])
+def test_block_kernel_request_falls_back_for_bf16_heads(fmt, monkeypatch):
+    """The block-split kernel covers bf16 and W8A16 only: a request for it with a bf16-head format
+    loads the default kernel, which then meets the gates."""
+    monkeypatch.setenv("AMK_KERNEL", "block")
+    shape = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0)
+    dec, orc, kv = build(shape, fmt, 340, 300, seed0=3)
+    assert dec.info().kernel == D.amk.AMK_KERNEL_WAVE
+    tok = W.gen_tokens(shape, 1, seed0=3)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 300, [], 4, first_token=tok, check_kv=True)
+    _assert_gates(res, f"block request fmt{fmt}")
+    dec.close()
+
+
 @pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied"])
 def test_w8a16_with_bf16_head(which):
     """Int8 projections with the lm_head kept bf16 (for a tied model the head reads the bf16
