@@ -1262,7 +1262,8 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
 
 // The blocks of kv head g each merge one slice of the head's G * HD outputs over its S splits
 // (log-sum-exp weights) and write it as tagged bf16 pairs. Thread t holds split t % SP of output
-// word w0 + t / SP (plus 512 / SP in the second round); SP = S rounded up to a power of two.
+// word w0 + t / SP (plus 512 / SP in a second round, run when the slice reaches it); SP = S rounded
+// up to a power of two.
 template <int HD>
 __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int layer) {
   const float NEG_INF = -__builtin_inff();
@@ -1302,19 +1303,23 @@ __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int laye
   const uint32_t to_tag = tag_of(p, layer, kTagO);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
+    if (w0 + r * wpr >= w1) break;  // uniform: no word of the slice falls in this round
     const int wd = w0 + r * wpr + tid / SP, sp = tid % SP;
     const bool v = wd < w1 && sp < S;
     const float mj = v ? mv[r] : NEG_INF;
     const float M = seg_max(mj, SP);
     const float e = (mj == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mj - M);  // base-2 maxima
+    // the three weighted sums are independent (one pass of reductions); the output is the
+    // values' sums over the sums' sum
     const float Ls = seg_sum(v ? lv[r] * e : 0.f, SP);
-    const float wgt = e * (1.0f / Ls);
-    const float o0 = seg_sum(v ? av[r][0] * wgt : 0.f, SP);
-    const float o1 = seg_sum(v ? av[r][1] * wgt : 0.f, SP);
+    const float s0 = seg_sum(v ? av[r][0] * e : 0.f, SP);
+    const float s1 = seg_sum(v ? av[r][1] * e : 0.f, SP);
     if (ok && v && sp == 0) {
+      const float inv = 1.0f / Ls;
       const int h = wd / (HD / 2), d = 2 * (wd - h * (HD / 2));
       st_tag(p.to + ((g * G + h) * HD + d) / 2,
-             static_cast<uint32_t>(f32_to_bf16(o0)) | (static_cast<uint32_t>(f32_to_bf16(o1)) << 16), to_tag);
+             static_cast<uint32_t>(f32_to_bf16(s0 * inv)) | (static_cast<uint32_t>(f32_to_bf16(s1 * inv)) << 16),
+             to_tag);
     }
   }
   return ok;
