@@ -24,12 +24,14 @@
 //    that stage's operand window (row scales, RoPE tables or residual) and its first two weight
 //    items into registers; attention issues its K/V loads before q arrives.
 //  * Activations: the GEMV input vector of a stage (RMSNorm output, attention output, SwiGLU
-//    output) is staged in LDS as fp32 holding bf16-rounded values, in a swizzled layout so the
-//    four 16-byte LDS reads of a lane per weight chunk are bank-conflict free.
+//    output) is staged in LDS as fp32 holding bf16-rounded values (as bf16 for int4 weights),
+//    in a swizzled layout so the 16-byte LDS reads of a lane per weight chunk are bank-conflict
+//    free.
 //  * W8A16: int8 codes convert with one v_cvt_f32_i32 (SDWA byte select, sign extend) per
 //    weight and feed an fp32 FMA; the per-row fp32 scale multiplies the wave-reduced sum.
-//    W4A16: two codes per byte; each converts with one v_cvt_off_f32_i4 on an SDWA byte select
-//    of the dword or of the dword shifted right by 4 (2.125 VALU per weight with the FMA).
+//    W4A16: sign-magnitude codes, eight per dword, laid out so that two masks turn a dword into
+//    eight fp8 (e4m3) subnormals of value q * 2^-9; gfx950's fp8-to-bf16 pair conversion and
+//    bf16 pair dot products then take two weights per instruction (1.375 VALU per weight).
 //  * Row pairs: rows are packed at load time so that rows i and i + hd/2 of one head (a RoPE
 //    pair) and rows n of gate and up (a SwiGLU pair) are adjacent; one wave computes both rows
 //    of a pair, so the RoPE / SwiGLU / residual epilogues need no cross-wave exchange.
@@ -293,23 +295,50 @@ struct GridBarrier {
 // ------------------------------------------------------------------------------------------
 // weight formats and the LDS layout of a GEMV input vector
 // ------------------------------------------------------------------------------------------
+// BITS per weight. A 1 KB weight chunk covers CW columns and lane L owns LC consecutive columns
+// of it (16 bytes). Per chunk the lane reads NR 16-byte words of activations, and one chunk's
+// activations span XCS floats of LDS.
 template <int FMT> struct Fmt;
-template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8; };  // bf16
-template <> struct Fmt<1> { static constexpr int BITS = 8, CW = 1024, LC = 16; };  // int8
-template <> struct Fmt<2> { static constexpr int BITS = 4, CW = 2048, LC = 32; };  // int4
-// A 1 KB weight chunk covers CW columns; lane L owns LC consecutive columns (16 bytes).
-// Column e is stored at chunk*CW + (k/4)*256 + L*4 + k%4, k = e's index inside the lane, so
-// the lane's k/4-th float4 sits at a 16-byte lane stride: conflict-free ds_read_b128.
+template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8, NR = 2, XCS = 512; };    // bf16
+template <> struct Fmt<1> { static constexpr int BITS = 8, CW = 1024, LC = 16, NR = 4, XCS = 1024; };  // int8
+template <> struct Fmt<2> { static constexpr int BITS = 4, CW = 2048, LC = 32, NR = 4, XCS = 1024; };  // int4
+// bf16 and int8 weights: the activations are fp32 in LDS. Column e is stored at chunk*CW +
+// (k/4)*256 + L*4 + k%4, k = e's index inside the lane, so the lane's k/4-th float4 sits at a
+// 16-byte lane stride: conflict-free ds_read_b128.
+// int4 weights: the activations are bf16 in LDS (they are bf16 values). The lane's d-th 16-byte
+// word holds its columns 8d .. 8d + 7 in order and sits at 16 * (d * 64 + L) bytes into the
+// chunk's 4 KB; swz16 gives the 16-bit index.
 template <int FMT>
 __device__ __forceinline__ int swz(int e) {
   constexpr int CW = Fmt<FMT>::CW, LC = Fmt<FMT>::LC;
   const int ch = e / CW, r = e - ch * CW, ln = r / LC, k = r - ln * LC;
   return ch * CW + (k >> 2) * 256 + ln * 4 + (k & 3);
 }
+__device__ __forceinline__ int swz16(int e) {
+  const int ch = e >> 11, r = e & 2047, ln = r >> 5, k = r & 31;
+  return ch * 2048 + (((k >> 3) * 64 + ln) << 3) + (k & 7);
+}
 template <int FMT>
 __device__ __forceinline__ int padded(int K) {
   constexpr int CW = Fmt<FMT>::CW;
   return (K + CW - 1) / CW * CW;
+}
+// Stores activation e (a bf16 value held in a float) into a GEMV input vector in LDS; put_x4
+// stores columns e .. e + 3 (e a multiple of 4).
+template <int FMT>
+__device__ __forceinline__ void put_x(float* xs, int e, float v) {
+  if constexpr (FMT == 2) reinterpret_cast<uint16_t*>(xs)[swz16(e)] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+  else xs[swz<FMT>(e)] = v;
+}
+template <int FMT>
+__device__ __forceinline__ void put_x4(float* xs, int e, f32x4 v) {
+  if constexpr (FMT == 2) {
+    const uint32_t lo = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+    const uint32_t hi = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(xs) + swz16(e)) = uint2{lo, hi};
+  } else {
+    *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = v;
+  }
 }
 
 // Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt 0): weight loads in
@@ -471,11 +500,10 @@ __device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint
     for (int b = 0; b < VB; ++b) {
       const int qi = q0 + b * kThreads + tid;
       if (qi < nq)
-        *reinterpret_cast<f32x4*>(xs + swz<FMT>(4 * qi)) =
-            f32x4{bf_hi(v[b].x), bf_hi(v[b].y), bf_hi(v[b].z), bf_hi(v[b].w)};
+        put_x4<FMT>(xs, 4 * qi, f32x4{bf_hi(v[b].x), bf_hi(v[b].y), bf_hi(v[b].z), bf_hi(v[b].w)});
     }
   }
-  for (int e = K + tid; e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  for (int e = K + tid; e < padded<FMT>(K); e += kThreads) put_x<FMT>(xs, e, 0.f);
   return true;
 }
 
@@ -510,11 +538,11 @@ __device__ __forceinline__ void rmsnorm_embed_to_lds(const KParams& p, const flo
   for (int b = 0; b < kNormVB; ++b) {
     const int e = 2 * (b * kThreads + tid);
     if (e < H) {
-      xs[swz<FMT>(e)] = round_bf16((xv[b].x * r) * wv[b].x);
-      xs[swz<FMT>(e + 1)] = round_bf16((xv[b].y * r) * wv[b].y);
+      put_x<FMT>(xs, e, round_bf16((xv[b].x * r) * wv[b].x));
+      put_x<FMT>(xs, e + 1, round_bf16((xv[b].y * r) * wv[b].y));
     }
   }
-  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) put_x<FMT>(xs, e, 0.f);
 }
 
 // xs <- RMSNorm of the residual x polled from its tagged words (tag `tag`), zero padded. The
@@ -545,11 +573,11 @@ __device__ __forceinline__ bool norm_from_x(const KParams& p, const float* __res
   for (int b = 0; b < kNormVB; ++b) {
     const int e = 2 * (b * kThreads + tid);
     if (e < H) {
-      xs[swz<FMT>(e)] = round_bf16((xv[b].x * r) * wv[b].x);
-      xs[swz<FMT>(e + 1)] = round_bf16((xv[b].y * r) * wv[b].y);
+      put_x<FMT>(xs, e, round_bf16((xv[b].x * r) * wv[b].x));
+      put_x<FMT>(xs, e + 1, round_bf16((xv[b].y * r) * wv[b].y));
     }
   }
-  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) put_x<FMT>(xs, e, 0.f);
   return ok;
 }
 
@@ -561,11 +589,11 @@ __device__ __forceinline__ bool vector_from_words(const KParams& p, const uint64
   const int ob = toff(p, src);
   const bool ok = poll_block<8>(p, K / 4, tag, [&](int qi) { return ob + 16 * qi; },
                                 [&](int, int qi, uint32_t a, uint32_t c) {
-                                  *reinterpret_cast<f32x4*>(xs + swz<FMT>(4 * qi)) =
-                                      f32x4{bf16_to_f32(a & 0xffffu), bf16_to_f32(a >> 16), bf16_to_f32(c & 0xffffu),
-                                            bf16_to_f32(c >> 16)};
+                                  put_x4<FMT>(xs, 4 * qi,
+                                              f32x4{bf16_to_f32(a & 0xffffu), bf16_to_f32(a >> 16),
+                                                    bf16_to_f32(c & 0xffffu), bf16_to_f32(c >> 16)});
                                 });
-  for (int e = K + opaque(threadIdx.x); e < padded<FMT>(K); e += kThreads) xs[swz<FMT>(e)] = 0.f;
+  for (int e = K + opaque(threadIdx.x); e < padded<FMT>(K); e += kThreads) put_x<FMT>(xs, e, 0.f);
   return ok;
 }
 
@@ -635,57 +663,52 @@ struct Cursor {
   }
 };
 
-// Signed int4 code in bits 3:0 of byte B of v, times 1/16 (v_cvt_off_f32_i4 on an SDWA byte
-// select: one VALU op per code).
-template <int B>
-__device__ __forceinline__ float i4_at(int v) {
-  float r;
-  if (B == 0) r = __builtin_amdgcn_cvt_off_f32_i4(v);
-  else if (B == 1) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
-  else if (B == 2) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
-  else asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
-  return r;
+// Eight int4 codes of one dword against their eight activations (bf16, in column order). Byte k
+// of the dword holds the magnitude of column k in bits 0..2 and its sign in bit 7, the
+// magnitude of column k + 4 in bits 4..6, and the sign of column (k - 1) mod 4 + 4 in bit 3.
+// So w & 0x87878787 and (w rotated right by 4) & 0x87878787 are four e4m3 codes each whose
+// values are exactly q * 2^-9 (exponent field zero: subnormals); each pair converts to a bf16
+// pair exactly and enters a bf16 pair dot product (exact products, fp32 sum). The epilogue
+// applies the factor 2^9.
+__device__ __forceinline__ float dot8_i4(uint32_t w, const i32x4 x, float acc) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  const uint32_t lo = w & 0x87878787u;
+  const uint32_t hi = __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;
+  // the pairs are taken from one 8-wide bf16 view of the word (this compiler drops the element
+  // index of a bit cast of one int lane to a bf16 pair)
+  const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, x);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
+                                        __builtin_shufflevector(xb, xb, 0, 1), acc, false);  // columns 0, 1
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
+                                        __builtin_shufflevector(xb, xb, 2, 3), acc, false);  // 2, 3
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
+                                        __builtin_shufflevector(xb, xb, 4, 5), acc, false);  // 4, 5
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true),
+                                        __builtin_shufflevector(xb, xb, 6, 7), acc, false);  // 6, 7
+  return acc;
 }
 
-// The activations of one slot: LC / 4 float4 reads per lane from the swizzled LDS vector.
+// The activations of one slot: NR 16-byte reads per lane from the swizzled LDS vector.
 template <int FMT>
 struct XSlot {
-  f32x4 v[Fmt<FMT>::LC / 4];
+  f32x4 v[Fmt<FMT>::NR];
 };
 template <int FMT>
 __device__ __forceinline__ void load_x(const float* __restrict__ xl, XSlot<FMT>& x) {
 #pragma unroll
-  for (int k = 0; k < Fmt<FMT>::LC / 4; ++k) x.v[k] = *reinterpret_cast<const f32x4*>(xl + k * 256);
+  for (int k = 0; k < Fmt<FMT>::NR; ++k) x.v[k] = *reinterpret_cast<const f32x4*>(xl + k * 256);
 }
 
 template <int FMT>
 __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const XSlot<FMT>& xs, float& a0,
                                           float& a1) {
   if constexpr (FMT == 2) {
-    // dword d holds columns 8d .. 8d + 7, column 8d + i in bits 4i .. 4i + 3; codes arrive as
-    // q / 16 (the row scale carries the 16)
+    // dword d holds the lane's columns 8d .. 8d + 7; read d of the slot holds their activations
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const f32x4 xa = xs.v[2 * d], xb = xs.v[2 * d + 1];
-      const int u0 = w0[d], u1 = w1[d];
-      const int h0 = static_cast<int>(static_cast<uint32_t>(u0) >> 4);
-      const int h1 = static_cast<int>(static_cast<uint32_t>(u1) >> 4);
-      a0 = __builtin_fmaf(i4_at<0>(u0), xa[0], a0);
-      a1 = __builtin_fmaf(i4_at<0>(u1), xa[0], a1);
-      a0 = __builtin_fmaf(i4_at<0>(h0), xa[1], a0);
-      a1 = __builtin_fmaf(i4_at<0>(h1), xa[1], a1);
-      a0 = __builtin_fmaf(i4_at<1>(u0), xa[2], a0);
-      a1 = __builtin_fmaf(i4_at<1>(u1), xa[2], a1);
-      a0 = __builtin_fmaf(i4_at<1>(h0), xa[3], a0);
-      a1 = __builtin_fmaf(i4_at<1>(h1), xa[3], a1);
-      a0 = __builtin_fmaf(i4_at<2>(u0), xb[0], a0);
-      a1 = __builtin_fmaf(i4_at<2>(u1), xb[0], a1);
-      a0 = __builtin_fmaf(i4_at<2>(h0), xb[1], a0);
-      a1 = __builtin_fmaf(i4_at<2>(h1), xb[1], a1);
-      a0 = __builtin_fmaf(i4_at<3>(u0), xb[2], a0);
-      a1 = __builtin_fmaf(i4_at<3>(u1), xb[2], a1);
-      a0 = __builtin_fmaf(i4_at<3>(h0), xb[3], a0);
-      a1 = __builtin_fmaf(i4_at<3>(h1), xb[3], a1);
+      const i32x4 x = __builtin_bit_cast(i32x4, xs.v[d]);
+      a0 = dot8_i4(static_cast<uint32_t>(w0[d]), x, a0);
+      a1 = dot8_i4(static_cast<uint32_t>(w1[d]), x, a1);
     }
   } else if constexpr (FMT == 1) {
 #pragma unroll
@@ -725,7 +748,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   A = 1.f;
   B = 0.f;
   if (k < g.pb) {
-    if (FMT != 0) A = Sc[row];  // int4: the epilogue applies the factor 16
+    if (FMT != 0) A = Sc[row];  // int4: the epilogue applies the factor 2^9
     if (EPI == EPI_RESID) {
       B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
                            : ld_payload(p.tx + row);
@@ -824,17 +847,17 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
                                              const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
                                              float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
                                              EpiState& st, XSlot<FMT>& xn) {
-  constexpr int CW = Fmt<FMT>::CW;
+  constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
     XSlot<FMT> xc;
     if constexpr (FMT == 1) {
-      load_x<FMT>(xlane + min(c.ch, g.nch - 1) * CW, xc);
+      load_x<FMT>(xlane + min(c.ch, g.nch - 1) * XCS, xc);
     } else {
       xc = xn;
       Cursor cn = c;
       cn.advance(g.cpp);
-      load_x<FMT>(xlane + min(cn.ch, g.nch - 1) * CW, xn);
+      load_x<FMT>(xlane + min(cn.ch, g.nch - 1) * XCS, xn);
     }
     // keep the scheduler from hoisting the conversions of all slots at once (register spills)
     __builtin_amdgcn_sched_barrier(0);
@@ -848,9 +871,9 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
         y0 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j));
         y1 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j + 1));
       }
-      if (FMT == 2) {  // the int4 products arrived as q / 16 (exact)
-        y0 *= 16.f;
-        y1 *= 16.f;
+      if (FMT == 2) {  // the int4 products arrived as q * 2^-9 (exact)
+        y0 *= 512.f;
+        y1 *= 512.f;
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));

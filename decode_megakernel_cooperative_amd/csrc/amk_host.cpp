@@ -143,6 +143,29 @@ int validate_config(const amk_config* c) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Eight int4 codes (q in [-7, 7], columns c .. c + 7) as one 32-bit word for the kernel's fp8
+// decode. Byte k holds |q_k| in bits 0..2 and the sign of q_k in bit 7, |q_(k+4)| in bits 4..6,
+// and the sign of q_((k+3) mod 4 + 4) in bit 3. Masking the word, and the word rotated right by 4,
+// with 0x87878787 then yields four e4m3 codes each whose values are q * 2^-9 in column order.
+uint32_t pack_int4_word(const int8_t* q) {
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int a = q[k], b = q[k + 4];
+    w |= static_cast<uint32_t>(a < 0 ? -a : a) << (8 * k);
+    w |= static_cast<uint32_t>(a < 0) << (8 * k + 7);
+    w |= static_cast<uint32_t>(b < 0 ? -b : b) << (8 * k + 4);
+    w |= static_cast<uint32_t>(b < 0) << ((8 * k + 11) % 32);
+  }
+  return w;
+}
+void unpack_int4_word(uint32_t w, int8_t* q) {
+  for (int k = 0; k < 4; ++k) {
+    const int a = static_cast<int>((w >> (8 * k)) & 7u), b = static_cast<int>((w >> (8 * k + 4)) & 7u);
+    q[k] = static_cast<int8_t>((w >> (8 * k + 7)) & 1u ? -a : a);
+    q[k + 4] = static_cast<int8_t>((w >> ((8 * k + 11) % 32)) & 1u ? -b : b);
+  }
+}
+
 // Row order of the packed QKV matrix: pair p = (head block hb, i) occupies rows 2p, 2p+1 and
 // holds source rows hb*hd + i and hb*hd + i + hd/2 (head blocks: nq query, nkv key, nkv value).
 // Returns the source (tensor offset 0 = q, 1 = k, 2 = v) and row for packed row r.
@@ -341,8 +364,8 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     return AMK_OK;
   };
   // Packs rows of one layer's matrix given a row map (packed row -> source pointer).
-  // bits: 16 (bf16 rows copied), 8 (int8 codes) or 4 (int4 codes, column c of a row in byte c / 2,
-  // the low nibble for even c, two's complement)
+  // bits: 16 (bf16 rows copied), 8 (int8 codes) or 4 (int4 codes, eight per 32-bit word in the
+  // sign-magnitude layout of pack_int4_word)
   auto pack_matrix = [&](int bits, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
                          const std::vector<const uint16_t*>& src_tensors,
                          auto&& row_source) -> int {
@@ -366,12 +389,12 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
         std::memcpy(codes.data() + r * cols, qc[w].data() + sr * cols, static_cast<size_t>(cols));
         scales[static_cast<size_t>(r)] = qs[w][static_cast<size_t>(sr)];
       }
-      if (bits == 4) {  // two codes per byte, in place (byte i is written after codes 2i, 2i + 1 are read)
-        const int64_t n = rows * cols / 2;
-        for (int64_t i = 0; i < n; ++i)
-          codes[static_cast<size_t>(i)] = static_cast<int8_t>(
-              (static_cast<uint8_t>(codes[static_cast<size_t>(2 * i)]) & 0x0F) |
-              ((static_cast<uint8_t>(codes[static_cast<size_t>(2 * i + 1)]) & 0x0F) << 4));
+      if (bits == 4) {  // eight codes per word, in place (word i is written after codes 8i .. 8i + 7 are read)
+        const int64_t n = rows * cols / 8;
+        for (int64_t i = 0; i < n; ++i) {
+          const uint32_t w = pack_int4_word(codes.data() + 8 * i);
+          std::memcpy(codes.data() + 4 * i, &w, 4);
+        }
       }
       int e = upload(dst_w, codes.data(), static_cast<size_t>(rows * cols * bits / 8));
       if (e) return e;
@@ -621,11 +644,11 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
   std::vector<float> alls(static_cast<size_t>(mrows));
   HIP_TRY(hipMemcpy(allc.data(), m->weights + wsrc, static_cast<size_t>(mrows * cols * bits / 8), hipMemcpyDeviceToHost));
   HIP_TRY(hipMemcpy(alls.data(), m->weights + ssrc, alls.size() * 4, hipMemcpyDeviceToHost));
-  if (bits == 4)  // unpack in place from the back: byte i holds codes 2i (low nibble) and 2i + 1
-    for (int64_t i = mrows * cols / 2 - 1; i >= 0; --i) {
-      const uint8_t b = static_cast<uint8_t>(allc[static_cast<size_t>(i)]);
-      allc[static_cast<size_t>(2 * i + 1)] = static_cast<int8_t>(static_cast<int8_t>(b & 0xF0) >> 4);
-      allc[static_cast<size_t>(2 * i)] = static_cast<int8_t>(static_cast<int8_t>(b << 4) >> 4);
+  if (bits == 4)  // unpack in place from the back: word i holds codes 8i .. 8i + 7
+    for (int64_t i = mrows * cols / 8 - 1; i >= 0; --i) {
+      uint32_t w;
+      std::memcpy(&w, allc.data() + 4 * i, 4);
+      unpack_int4_word(w, allc.data() + 8 * i);
     }
   for (int64_t r = 0; r < mrows; ++r) {
     int w = 0;

@@ -44,7 +44,7 @@ extern "C" {
 #define AMK_W8A16 1 /* weights int8, one fp32 scale per output row; activations bf16      */
 #define AMK_W8A16_BF16_HEAD 2 /* AMK_W8A16 projections, lm_head kept bf16 (for a tied model the
                                  head reads the bf16 embedding table; no quantized copy)      */
-#define AMK_W4A16 3 /* projections int4 (two codes per byte), one fp32 scale per output row;
+#define AMK_W4A16 3 /* projections int4 (eight codes per word), one fp32 scale per output row;
                        lm_head kept bf16 as in AMK_W8A16_BF16_HEAD; activations bf16           */
 
 /* Model description. Weights follow HuggingFace LlamaForCausalLM: pre-norm RMSNorm,
@@ -121,8 +121,9 @@ typedef struct {
  * AMK_W4A16 quantizes the projections with amk_quantize_int4 and keeps the lm_head bf16 (the
  * pages' int4 weight-only variant: lossy, 2.42x less weight traffic than bf16; gist.science
  * explainer, Technical Summary > Key Contributions; this format streams 1/2.44 of the bf16
- * weight bytes of a SmolLM2-135M or Llama-3.2-1B shape). Device row layout: code of column c
- * in byte c / 2, low nibble for even c, two's complement.
+ * weight bytes of a SmolLM2-135M or Llama-3.2-1B shape). Device row layout: columns 8i .. 8i + 7
+ * in 32-bit word i; byte k of a word holds |q| of column k in bits 0..2 and its sign in bit 7,
+ * |q| of column k + 4 in bits 4..6, and the sign of column (k + 3) mod 4 + 4 in bit 3.
  * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
  * *out receives a model handle owned by the library until amk_free.
  * Errors: INVALID_ARG (null pointers, wrong n_tensors), UNSUPPORTED (shape checks: head_dim
