@@ -299,15 +299,16 @@ struct GridBarrier {
 // of it (16 bytes). Per chunk the lane reads NR 16-byte words of activations, and one chunk's
 // activations span XCS floats of LDS.
 template <int FMT> struct Fmt;
-template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8, NR = 2, XCS = 512; };    // bf16
+template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8, NR = 1, XCS = 256; };    // bf16
 template <> struct Fmt<1> { static constexpr int BITS = 8, CW = 1024, LC = 16, NR = 4, XCS = 1024; };  // int8
 template <> struct Fmt<2> { static constexpr int BITS = 4, CW = 2048, LC = 32, NR = 4, XCS = 1024; };  // int4
-// bf16 and int8 weights: the activations are fp32 in LDS. Column e is stored at chunk*CW +
-// (k/4)*256 + L*4 + k%4, k = e's index inside the lane, so the lane's k/4-th float4 sits at a
-// 16-byte lane stride: conflict-free ds_read_b128.
-// int4 weights: the activations are bf16 in LDS (they are bf16 values). The lane's d-th 16-byte
-// word holds its columns 8d .. 8d + 7 in order and sits at 16 * (d * 64 + L) bytes into the
-// chunk's 4 KB; swz16 gives the 16-bit index.
+// int8 weights: the activations are fp32 in LDS. Column e is stored at chunk*CW + (k/4)*256 +
+// L*4 + k%4, k = e's index inside the lane, so the lane's k/4-th float4 sits at a 16-byte lane
+// stride: conflict-free ds_read_b128.
+// bf16 and int4 weights: the activations are bf16 in LDS (they are bf16 values). For bf16 the
+// vector is in column order (lane L's eight columns are its 16-byte word). For int4 the lane's
+// d-th 16-byte word holds its columns 8d .. 8d + 7 in order and sits at 16 * (d * 64 + L) bytes
+// into the chunk's 4 KB; swz16 gives the 16-bit index.
 template <int FMT>
 __device__ __forceinline__ int swz(int e) {
   constexpr int CW = Fmt<FMT>::CW, LC = Fmt<FMT>::LC;
@@ -328,14 +329,15 @@ __device__ __forceinline__ int padded(int K) {
 template <int FMT>
 __device__ __forceinline__ void put_x(float* xs, int e, float v) {
   if constexpr (FMT == 2) reinterpret_cast<uint16_t*>(xs)[swz16(e)] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+  else if constexpr (FMT == 0) reinterpret_cast<uint16_t*>(xs)[e] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
   else xs[swz<FMT>(e)] = v;
 }
 template <int FMT>
 __device__ __forceinline__ void put_x4(float* xs, int e, f32x4 v) {
-  if constexpr (FMT == 2) {
+  if constexpr (FMT != 1) {
     const uint32_t lo = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
     const uint32_t hi = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(xs) + swz16(e)) = uint2{lo, hi};
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(xs) + (FMT == 2 ? swz16(e) : e)) = uint2{lo, hi};
   } else {
     *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = v;
   }
@@ -721,18 +723,18 @@ __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const 
       }
     }
   } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 x = xs.v[h];
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int u0 = w0[2 * h + d], u1 = w1[2 * h + d];
-        a0 = __builtin_fmaf(bf_lo(u0), x[2 * d], a0);
-        a0 = __builtin_fmaf(bf_hi(u0), x[2 * d + 1], a0);
-        a1 = __builtin_fmaf(bf_lo(u1), x[2 * d], a1);
-        a1 = __builtin_fmaf(bf_hi(u1), x[2 * d + 1], a1);
-      }
-    }
+    // dword d holds the bf16 weights of columns 2d, 2d + 1; so does dword d of the activations
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    const bf16x8_t x = __builtin_bit_cast(bf16x8_t, xs.v[0]);
+    const bf16x8_t u0 = __builtin_bit_cast(bf16x8_t, w0), u1 = __builtin_bit_cast(bf16x8_t, w1);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u0, u0, 0, 1), __builtin_shufflevector(x, x, 0, 1), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u1, u1, 0, 1), __builtin_shufflevector(x, x, 0, 1), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u0, u0, 2, 3), __builtin_shufflevector(x, x, 2, 3), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u1, u1, 2, 3), __builtin_shufflevector(x, x, 2, 3), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u0, u0, 4, 5), __builtin_shufflevector(x, x, 4, 5), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u1, u1, 4, 5), __builtin_shufflevector(x, x, 4, 5), a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u0, u0, 6, 7), __builtin_shufflevector(x, x, 6, 7), a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(u1, u1, 6, 7), __builtin_shufflevector(x, x, 6, 7), a1, false);
   }
 }
 
