@@ -21,7 +21,7 @@ The reading used here is the same rule at four bits: symmetric per output row, s
 fp32(amax_n / 7) by IEEE division, q_nk = clamp(round_half_even(fp32(w_nk / s_n)), -7, 7), a
 zero row gives s_n = 0 and q_n = 0. With the lm_head (and a tied embedding) kept in bf16 this
 streams 1 / 2.44 of the bf16 weight bytes for SmolLM2-135M and for Llama-3.2-1B, which matches
-the pages' figure to its precision. Codes are stored two per byte on the GPU side; here they are
+the pages' figure to its precision. Codes take four bits each on the GPU side; here they are
 kept one per int8.
 """
 import numpy as np

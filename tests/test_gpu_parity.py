@@ -193,7 +193,7 @@ def test_w8a16_with_bf16_head(which):
 
 @pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied"])
 def test_w4a16_parity(which):
-    """Int4 per-row projections (two codes per byte) with the lm_head kept bf16: every
+    """Int4 per-row projections (four bits per code) with the lm_head kept bf16: every
     projection's codes and scales bit-exact against the oracle's quantizer, then the logit and
     greedy gates over prompt and greedy steps (multi-split attention for the prefilled shape)."""
     if which == "smollm2-tied":
