@@ -27,12 +27,10 @@ AMK_BF16 = 0
 AMK_W8A16 = 1
 AMK_W8A16_BF16_HEAD = 2
 AMK_W4A16 = 3
-AMK_KERNEL_WAVE = 0
-AMK_KERNEL_BLOCK = 1
 
-EXPORTED = ("amk_load_weights", "amk_decode_step", "amk_decode_step_greedy", "amk_sync", "amk_kv_cache_bytes", "amk_get_info",
-            "amk_export_quantized", "amk_quantize_int8", "amk_quantize_int4", "amk_bench_barrier", "amk_set_spin_limit",
-            "amk_set_trace", "amk_free", "amk_status_string")
+EXPORTED = ("amk_validate_config", "amk_load_weights", "amk_decode_step", "amk_decode_step_greedy", "amk_sync",
+            "amk_kv_cache_bytes", "amk_get_info", "amk_export_quantized", "amk_quantize_int8", "amk_quantize_int4",
+            "amk_set_spin_limit", "amk_set_trace", "amk_set_dump", "amk_free", "amk_status_string")
 
 
 class AmkError(RuntimeError):
@@ -55,7 +53,7 @@ class amk_info(ctypes.Structure):
     _fields_ = [("grid_blocks", ctypes.c_int32), ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("handoffs_per_step", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("scratch_bytes", ctypes.c_int64), ("max_splits", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("kernel", ctypes.c_int32)]
+                ("dump_layer_floats", ctypes.c_int64), ("dump_floats", ctypes.c_int64)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -70,6 +68,7 @@ def lib() -> ctypes.CDLL:
                                     "`python -m decode_megakernel_cooperative_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.amk_validate_config.argtypes = [ctypes.POINTER(amk_config), i32]
         L.amk_load_weights.argtypes = [ctypes.POINTER(amk_config), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]
         L.amk_decode_step.argtypes = [vp, i32, i32, vp, vp, vp]
         L.amk_decode_step_greedy.argtypes = [vp, vp, i32, vp, vp, vp, vp]
@@ -80,9 +79,9 @@ def lib() -> ctypes.CDLL:
         L.amk_export_quantized.argtypes = [vp, i32, vp, vp]
         L.amk_quantize_int8.argtypes = [vp, i64, i64, vp, vp]
         L.amk_quantize_int4.argtypes = [vp, i64, i64, vp, vp]
-        L.amk_bench_barrier.argtypes = [i32, ctypes.POINTER(ctypes.c_float)]
         L.amk_set_spin_limit.argtypes = [vp, ctypes.c_uint64]
         L.amk_set_trace.argtypes = [vp, vp, i32]
+        L.amk_set_dump.argtypes = [vp, vp, i64]
         L.amk_free.argtypes = [vp]
         L.amk_status_string.argtypes = [ctypes.c_int]
         L.amk_status_string.restype = ctypes.c_char_p
@@ -193,12 +192,6 @@ def amk_quantize_int4(w_bits: np.ndarray):
     return codes, scales
 
 
-def amk_bench_barrier(iters: int) -> float:
-    us = ctypes.c_float()
-    _check(lib().amk_bench_barrier(int(iters), ctypes.byref(us)))
-    return us.value
-
-
 def amk_set_spin_limit(model: int, ticks: int) -> None:
     _check(lib().amk_set_spin_limit(model, int(ticks)))
 
@@ -207,6 +200,18 @@ def amk_set_trace(model: int, trace, events_per_block: int) -> None:
     """trace: device uint64/int64 tensor [grid_blocks][events_per_block], or None to stop tracing."""
     ptr = trace.data_ptr() if trace is not None else None
     _check(lib().amk_set_trace(model, ptr, int(events_per_block)))
+
+
+def amk_set_dump(model: int, dump) -> None:
+    """dump: device fp32 tensor of at least amk_get_info(model).dump_floats elements, or None."""
+    ptr = dump.data_ptr() if dump is not None else None
+    n = dump.numel() if dump is not None else 0
+    _check(lib().amk_set_dump(model, ptr, int(n)))
+
+
+def amk_validate_config(cfg: amk_config, compute_units: int) -> None:
+    """Raises AmkError if the library would refuse this model on a device with that many CUs."""
+    _check(lib().amk_validate_config(ctypes.byref(cfg), int(compute_units)))
 
 
 def amk_free(model: int) -> None:

@@ -43,7 +43,7 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     common = ["-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
     kobjs = []
-    for src in ("amk_decode.hip", "amk_stream.hip"):
+    for src in ("amk_decode.hip",):
         kobj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         _run([cc, f"--offload-arch={ARCH}", "-O3", *common,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -51,24 +51,6 @@
 
 #include "amk_kparams.h"
 
-#ifndef AMK_FINE_TRACE
-#define AMK_FINE_TRACE 0  // 1: extra trace stamps inside every layer (stage-internal timing)
-#endif
-#ifndef AMK_KCG
-#define AMK_KCG 2         // 1 KB chunk slots per GEMV item (per row)
-#endif
-#ifndef AMK_STRIDED
-#define AMK_STRIDED 2     // how a GEMV stage's row pairs map to the NW waves of the grid:
-                          // 2: wave w of block b is stream s = w * blocks + b and takes pairs s,
-                          //    s + NW, ...: at any moment the grid streams one sliding window of
-                          //    the matrix, consecutive pairs going to consecutive blocks (and so to
-                          //    different XCDs); 1: the same with s = b * 8 + w; 0: a contiguous
-                          //    range of pairs per wave
-#endif
-#ifndef AMK_PREFETCH_ITEMS
-#define AMK_PREFETCH_ITEMS 2  // GEMV items issued before the barrier in front of a stage (1 or 2)
-#endif
-
 namespace amk {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -230,69 +212,6 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// grid barrier (the library's barrier microbenchmark only: the decode kernel synchronises by
-// tagged hand-offs, whose cost this measures a lower bound against)
-// ------------------------------------------------------------------------------------------
-struct GridBarrier {
-  unsigned* ctr;
-  unsigned base;   // barriers completed by earlier launches
-  unsigned n;      // barriers completed in this launch
-  uint64_t limit;
-  unsigned* err;
-  uint64_t* trace; // optional per-block timestamps (entry, then arrival/exit of every barrier)
-  int ev;
-
-  __device__ __forceinline__ void stamp() {
-    if (trace != nullptr && threadIdx.x == 0) trace[ev] = wall_clock64();
-    ++ev;
-  }
-
-  // Arrival: waits for this block's stores (s_waitcnt 0 per wave, then the workgroup
-  // barrier) and adds one to the block's arrival counter. Loads issued after arrive() and
-  // before wait() overlap the wait (the next stage's weights are prefetched there).
-  __device__ __forceinline__ void arrive() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    stamp();
-    ++n;
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(ctr + (blockIdx.x & (kBarrierCtrs - 1)) * kCtrStride, 1u,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // Wait until every block has arrived n times. Returns false if the step must be abandoned
-  // (timeout here or an error raised by another block).
-  __device__ __forceinline__ bool wait(int* abort_lds) {
-    const unsigned tid = threadIdx.x;
-    if (tid < kBarrierCtrs && tid < gridDim.x) {
-      const unsigned per = (gridDim.x - tid + kBarrierCtrs - 1) / kBarrierCtrs;
-      const unsigned target = (base + n) * per;
-      const uint64_t t0 = wall_clock64();
-      unsigned it = 0;
-      bool bad = false;
-      while (static_cast<int>(ldc(ctr + tid * kCtrStride) - target) < 0) {
-        __builtin_amdgcn_s_sleep(1);
-        if (((++it) & 31u) == 0) {
-          if (ldc(err) != 0u) { bad = true; break; }
-          if (wall_clock64() - t0 > limit) { stc(err, kErrTimeout); bad = true; break; }
-        }
-      }
-      if (bad) *abort_lds = 1;
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    stamp();
-    return *abort_lds == 0;
-  }
-
-  __device__ __forceinline__ bool sync(int* abort_lds) {
-    arrive();
-    return wait(abort_lds);
-  }
-};
-
-// ------------------------------------------------------------------------------------------
 // weight formats and the LDS layout of a GEMV input vector
 // ------------------------------------------------------------------------------------------
 // BITS per weight. A 1 KB weight chunk covers CW columns and lane L owns LC consecutive columns
@@ -377,13 +296,29 @@ __device__ __forceinline__ int step_token(const KParams& p) {
   return (t >= 0 && t < p.V) ? t : 0;
 }
 
-// stage-internal stamps (AMK_FINE_TRACE builds only): slot k of layer l after the stage stamps
-__device__ __forceinline__ void fstamp(const KParams& p, int l, int k) {
-  if (AMK_FINE_TRACE && p.trace != nullptr && threadIdx.x == 0)
-    p.trace[static_cast<size_t>(blockIdx.x) * p.trace_stride + 3 + 11 * p.L + l * 16 + k] = wall_clock64();
-}
 __device__ __forceinline__ int toff(const KParams& p, const uint64_t* buf) {
   return static_cast<int>(reinterpret_cast<const uint8_t*>(buf) - reinterpret_cast<const uint8_t*>(p.tagged));
+}
+
+// Raises device error `code` unless another one was raised first in this launch: the first
+// raiser also writes the code to the pinned host word, where the next step call finds it without
+// synchronising (exactly one write per failed launch).
+__device__ __forceinline__ void raise_error(const KParams& p, unsigned code) {
+  unsigned expected = 0u;
+  if (__hip_atomic_compare_exchange_strong(p.err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+    __hip_atomic_store(p.herr, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Per-stage dump of layer l (see amk_set_dump): the slots in the order of the dump layout.
+enum { kDH = 0, kDQKV, kDQ, kDO, kDWO, kDXO, kDH2, kDGU, kDM, kDWD, kDXD };
+__device__ __forceinline__ float* dump_at(const KParams& p, int l, int slot) {
+  if (p.dump == nullptr) return nullptr;
+  const int H = p.H, QD = p.nq * p.hd, QKV = QD + 2 * p.nkv * p.hd, F = p.F;
+  const int off[11] = {0, H, H + QKV, H + QKV + QD, H + QKV + 2 * QD, 2 * H + QKV + 2 * QD, 3 * H + QKV + 2 * QD,
+                       4 * H + QKV + 2 * QD, 4 * H + QKV + 2 * QD + 2 * F, 4 * H + QKV + 2 * QD + 3 * F,
+                       5 * H + QKV + 2 * QD + 3 * F};
+  return p.dump + static_cast<int64_t>(l) * p.dump_stride + (l < p.L ? off[slot] : 0);
 }
 
 // Bound of a hand-off wait, checked after its reload number `it`: false once the step must be
@@ -394,7 +329,7 @@ __device__ __forceinline__ bool wait_ok(const KParams& p, unsigned it, uint64_t 
   const bool round16 = (it & 15u) == 0;
   if (round16 && ldc(p.err) != 0u) return false;
   if ((round16 || it == 2) && wall_clock64() - t_start > p.spin_limit) {
-    stc(p.err, kErrTimeout);
+    raise_error(p, kErrTimeout);
     return false;
   }
   return true;
@@ -511,11 +446,32 @@ __device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint
 
 constexpr int kNormVB = 8;  // RMSNorm inputs up to 2 * 8 * 512 = 8192 elements
 
+// xs <- bf16((x * r) * w) for the thread's element pairs e = 2 (b * 512 + tid), zero padded to
+// whole weight chunks; block 0 also writes the values to the dump slot dh (when dumping).
+template <int FMT>
+__device__ __forceinline__ void norm_out(int H, float r, const float2 (&xv)[kNormVB], const float2 (&wv)[kNormVB],
+                                         float* xs, float* dh) {
+#pragma clang fp contract(off)
+  const int tid = opaque(threadIdx.x);
+  const bool dump = dh != nullptr && blockIdx.x == 0;
+#pragma unroll
+  for (int b = 0; b < kNormVB; ++b) {
+    const int e = 2 * (b * kThreads + tid);
+    if (e < H) {
+      const float h0 = round_bf16((xv[b].x * r) * wv[b].x), h1 = round_bf16((xv[b].y * r) * wv[b].y);
+      put_x<FMT>(xs, e, h0);
+      put_x<FMT>(xs, e + 1, h1);
+      if (dump) *reinterpret_cast<float2*>(dh + e) = float2{h0, h1};
+    }
+  }
+  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) put_x<FMT>(xs, e, 0.f);
+}
+
 // xs <- bf16((x * rsqrt(mean(x^2) + eps)) * w) for the first layer, x = the bf16 embedding row,
 // zero padded to whole weight chunks.
 template <int FMT>
 __device__ __forceinline__ void rmsnorm_embed_to_lds(const KParams& p, const float* __restrict__ w, float* xs,
-                                                     float* red) {
+                                                     float* red, float* dh) {
 #pragma clang fp contract(off)
   const int H = p.H, tid = opaque(threadIdx.x);
   const uint16_t* row = p.embed + static_cast<size_t>(step_token(p)) * H;
@@ -536,22 +492,14 @@ __device__ __forceinline__ void rmsnorm_embed_to_lds(const KParams& p, const flo
   for (int b = 0; b < kNormVB; ++b) ss += xv[b].x * xv[b].x + xv[b].y * xv[b].y;
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + p.eps);
-#pragma unroll
-  for (int b = 0; b < kNormVB; ++b) {
-    const int e = 2 * (b * kThreads + tid);
-    if (e < H) {
-      put_x<FMT>(xs, e, round_bf16((xv[b].x * r) * wv[b].x));
-      put_x<FMT>(xs, e + 1, round_bf16((xv[b].y * r) * wv[b].y));
-    }
-  }
-  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) put_x<FMT>(xs, e, 0.f);
+  norm_out<FMT>(H, r, xv, wv, xs, dh);
 }
 
 // xs <- RMSNorm of the residual x polled from its tagged words (tag `tag`), zero padded. The
 // weights are loaded with the poll, in the same round trip. Returns false if abandoned.
 template <int FMT>
 __device__ __forceinline__ bool norm_from_x(const KParams& p, const float* __restrict__ w, uint32_t tag, float* xs,
-                                            float* red) {
+                                            float* red, float* dh) {
 #pragma clang fp contract(off)
   const int H = p.H, tid = opaque(threadIdx.x);
   float2 xv[kNormVB], wv[kNormVB];
@@ -571,15 +519,7 @@ __device__ __forceinline__ bool norm_from_x(const KParams& p, const float* __res
   for (int b = 0; b < kNormVB; ++b) ss += xv[b].x * xv[b].x + xv[b].y * xv[b].y;
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / static_cast<float>(H) + p.eps);
-#pragma unroll
-  for (int b = 0; b < kNormVB; ++b) {
-    const int e = 2 * (b * kThreads + tid);
-    if (e < H) {
-      put_x<FMT>(xs, e, round_bf16((xv[b].x * r) * wv[b].x));
-      put_x<FMT>(xs, e + 1, round_bf16((xv[b].y * r) * wv[b].y));
-    }
-  }
-  for (int e = H + tid; e < padded<FMT>(H); e += kThreads) put_x<FMT>(xs, e, 0.f);
+  norm_out<FMT>(H, r, xv, wv, xs, dh);
   return ok;
 }
 
@@ -587,13 +527,15 @@ __device__ __forceinline__ bool norm_from_x(const KParams& p, const float* __res
 // padded. Four consecutive elements land in one float4 of the swizzled layout.
 template <int FMT>
 __device__ __forceinline__ bool vector_from_words(const KParams& p, const uint64_t* src, int K, uint32_t tag,
-                                                  float* xs) {
+                                                  float* xs, float* dv) {
   const int ob = toff(p, src);
+  const bool dump = dv != nullptr && blockIdx.x == 0;
   const bool ok = poll_block<8>(p, K / 4, tag, [&](int qi) { return ob + 16 * qi; },
                                 [&](int, int qi, uint32_t a, uint32_t c) {
-                                  put_x4<FMT>(xs, 4 * qi,
-                                              f32x4{bf16_to_f32(a & 0xffffu), bf16_to_f32(a >> 16),
-                                                    bf16_to_f32(c & 0xffffu), bf16_to_f32(c >> 16)});
+                                  const f32x4 v{bf16_to_f32(a & 0xffffu), bf16_to_f32(a >> 16),
+                                                bf16_to_f32(c & 0xffffu), bf16_to_f32(c >> 16)};
+                                  put_x4<FMT>(xs, 4 * qi, v);
+                                  if (dump) *reinterpret_cast<f32x4*>(dv + 4 * qi) = v;
                                 });
   for (int e = K + opaque(threadIdx.x); e < padded<FMT>(K); e += kThreads) put_x<FMT>(xs, e, 0.f);
   return ok;
@@ -604,7 +546,7 @@ __device__ __forceinline__ bool vector_from_words(const KParams& p, const uint64
 // ------------------------------------------------------------------------------------------
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
-constexpr int kCG = AMK_KCG;  // chunk slots per item: 2 rows x kCG x 16 B dwordx4 loads per lane
+constexpr int kCG = 2;  // chunk slots per item: 2 rows x kCG x 16 B dwordx4 loads per lane
 constexpr int kSeg = 32; // pairs per operand window (lane j holds the operand of packed row 2*base + j)
 
 // Registers that carry a GEMV stage's operand window and first two items across the wait for
@@ -628,29 +570,22 @@ struct GemvPlan {
 };
 __device__ __forceinline__ int pidx(const GemvPlan& g, int k) { return g.st0 + k * g.sst; }
 
-// Pairs are split over the waves in units of `unit` pairs (2 for gate/up, so a wave's SwiGLU
-// outputs fill whole two-value exchange words).
+// Pairs are split over all waves of the grid by a strided map: wave w of block b is stream
+// s = w * blocks + b and takes pairs s, s + NW, s + 2 NW, ... (NW = waves in the grid). At any
+// moment the grid streams one sliding window of the matrix, consecutive pairs going to
+// consecutive blocks (and so to different XCDs), and block b holds pair b of every stage.
 template <int FMT>
-__device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave, int unit) {
+__device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave) {
   GemvPlan g;
   g.RB = K * Fmt<FMT>::BITS / 8;
   g.nch = (g.RB + 1023) >> 10;
   g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
-  const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
-  if (AMK_STRIDED) {
-    const int sw = AMK_STRIDED == 2 ? wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x) : gw;
-    g.pa = 0;
-    g.pb = sw < npairs ? (npairs - sw + NW - 1) / NW : 0;
-    g.st0 = sw;
-    g.sst = NW;
-    (void)unit;
-    return g;
-  }
-  const int nu = npairs / unit;
-  g.pa = unit * static_cast<int>((static_cast<int64_t>(nu) * gw) / NW);
-  g.pb = unit * static_cast<int>((static_cast<int64_t>(nu) * (gw + 1)) / NW);
-  g.st0 = 0;
-  g.sst = 1;
+  const int NW = gridDim.x * kWaves;
+  const int sw = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
+  g.pa = 0;
+  g.pb = sw < npairs ? (npairs - sw + NW - 1) / NW : 0;
+  g.st0 = sw;
+  g.sst = NW;
   return g;
 }
 
@@ -772,10 +707,11 @@ struct EpiState {
 
 // Runs in lane 0 for one finished row pair: scale (applied by the caller), then q / K / V with
 // RoPE (and the K/V append to the cache), the residual add, SwiGLU, or the logits. Values that
-// cross blocks are written as tagged words (tag tg); a SwiGLU output is one 32-bit word.
+// cross blocks are written as tagged words (tag tg); a SwiGLU output is one 32-bit word. dp is
+// the stage's dump slot (null unless dumping): the GEMV outputs and what the epilogue derives.
 template <int EPI>
 __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, float y0, float y1, float b0, float b1,
-                                         uint32_t tg, EpiState& st) {
+                                         uint32_t tg, EpiState& st, float* dp) {
 #pragma clang fp contract(off)
   if (EPI == EPI_QKV) {
     const int half = p.hd >> 1;
@@ -785,6 +721,15 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
       const float c = b0, s = b1;
       a = y0 * c - y1 * s;
       b = y1 * c + y0 * s;
+    }
+    if (dp != nullptr) {  // rows hb * hd + i and hb * hd + i + half of q | k | v; then q rotated
+      const int QKV = (p.nq + 2 * p.nkv) * p.hd;
+      dp[hb * p.hd + i] = y0;
+      dp[hb * p.hd + i + half] = y1;
+      if (hb < p.nq) {
+        dp[QKV + hb * p.hd + i] = a;
+        dp[QKV + hb * p.hd + i + half] = b;
+      }
     }
     if (hb < p.nq) {
       st_tag(p.tq + hb * p.hd + i, __float_as_uint(a), tg);
@@ -799,11 +744,22 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
       st_tag(p.tkv + (kvs * p.nkv + g) * half + i, static_cast<uint32_t>(ba) | (static_cast<uint32_t>(bb) << 16), tg);
     }
   } else if (EPI == EPI_RESID) {
-    st_tag(p.tx + 2 * pr, __float_as_uint(b0 + y0), tg);
-    st_tag(p.tx + 2 * pr + 1, __float_as_uint(b1 + y1), tg);
+    const float x0 = b0 + y0, x1 = b1 + y1;
+    st_tag(p.tx + 2 * pr, __float_as_uint(x0), tg);
+    st_tag(p.tx + 2 * pr + 1, __float_as_uint(x1), tg);
+    if (dp != nullptr) {  // projection output, then the residual after it
+      *reinterpret_cast<float2*>(dp + 2 * pr) = float2{y0, y1};
+      *reinterpret_cast<float2*>(dp + p.H + 2 * pr) = float2{x0, x1};
+    }
   } else if (EPI == EPI_SWIGLU) {
     const float m = (y0 / (1.0f + expf(-y0))) * y1;
-    st_tag16(reinterpret_cast<uint32_t*>(p.tm) + pr, f32_to_bf16(m), tg);
+    const uint16_t mb = f32_to_bf16(m);
+    st_tag16(reinterpret_cast<uint32_t*>(p.tm) + pr, mb, tg);
+    if (dp != nullptr) {  // gate, up, then the SwiGLU output
+      dp[pr] = y0;
+      dp[p.F + pr] = y1;
+      dp[2 * p.F + pr] = bf16_to_f32(mb);
+    }
   } else {
     if (p.logits != nullptr) {
       p.logits[2 * pr] = y0;
@@ -848,7 +804,7 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
                                              const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
                                              float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
-                                             EpiState& st, XSlot<FMT>& xn) {
+                                             EpiState& st, XSlot<FMT>& xn, float* dp) {
   constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
@@ -879,7 +835,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
       }
       const float b0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j));
       const float b1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wB), j + 1));
-      if (__lane_id() == 0) epilogue<EPI>(p, layer, pidx(g, base + c.k), y0, y1, b0, b1, tg, st);
+      if (__lane_id() == 0) epilogue<EPI>(p, layer, pidx(g, base + c.k), y0, y1, b0, b1, tg, st, dp);
     }
     c.advance(g.cpp);
   }
@@ -902,9 +858,9 @@ template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
                                               GemvRegs& R) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), 1);
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
-  gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, AMK_PREFETCH_ITEMS > 1, R);
+  gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, true, R);
 }
 
 // Runs the stage. Items alternate between the two register buffers, each refilled two items
@@ -914,8 +870,8 @@ __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* _
 template <int FMT, int EPI>
 __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __restrict__ W,
                                          const float* __restrict__ Sc, int K, int npairs, const float* xs,
-                                         int layer, bool rfe, GemvRegs& R, uint32_t tg) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id(), 1);
+                                         int layer, bool rfe, GemvRegs& R, uint32_t tg, float* dp) {
+  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
   EpiState st{-__builtin_inff(), 0x7fffffff};
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   const float* xlane = xs + __lane_id() * 4;
@@ -925,22 +881,14 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
     const int items = (np * g.cpp + kCG - 1) / kCG;
     Cursor ci{0, 0}, cc{0, 0};
     for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
-    if (AMK_PREFETCH_ITEMS > 1 || base != g.pa) {
-      for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
-    } else {
-      gemv_issue(rs, g, base, np, ci, R.b0, R.b1);  // second item was not prefetched
-    }
+    for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
     float acc0 = 0.f, acc1 = 0.f;
     XSlot<FMT> xn;
     load_x<FMT>(xlane, xn);  // slot 0 of the segment is chunk 0
-    if (EPI == EPI_QKV) fstamp(p, layer, 12);
     for (int it = 0; it < items; it += 2) {
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn);
-      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 13);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn, dp);
       gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
-      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 14);
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn);
-      if (EPI == EPI_QKV && it == 0) fstamp(p, layer, 15);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn, dp);
       gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
     }
   }
@@ -1084,7 +1032,6 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       attn_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
     };
 
-    fstamp(p, layer, 0);
     // scores are kept in base-2 units (q pre-scaled by log2(e) / sqrt(HD)), so every softmax
     // weight is one exp2
     const float qscale = p.attn_scale * 1.4426950408889634f;
@@ -1178,7 +1125,6 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     for (int gb = wave; gb < ngroups; gb += 2 * step) {
       patch_pos(gb, KA, VA);
       compute(gb, KA, VA);
-      if (gb == wave) fstamp(p, layer, 1);
       load(gb + 2 * step, KA, VA);
       if (gb + step < ngroups) {  // uniform
         patch_pos(gb + step, KB, VB);
@@ -1189,7 +1135,6 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
 
     // every row's state into LDS (each row saw its own positions); rows that saw none hold
     // max -inf and zero sums
-    fstamp(p, layer, 2);
     float* row = wp + (wave * Lds::PPW + ri) * GMAX * RS;
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
@@ -1204,7 +1149,6 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
     }
   }
   wg_barrier();
-  fstamp(p, layer, 3);
   if (!a.active) return;
 
   // wave h < G: the head's block max M over the R rows, each row's weight 2^(m - M) and the
@@ -1324,7 +1268,6 @@ __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int laye
           av[bq >> 1][1] = __uint_as_float(x1);
         }
       });
-  fstamp(p, layer, 4);
   const uint32_t to_tag = tag_of(p, layer, kTagO);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -1461,7 +1404,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   if (err0 != 0u) return;
   if (p.token_dev != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
     const int t = *p.token_dev;
-    if (t < 0 || t >= p.V) stc(p.err, kErrBadToken);  // the step decodes token 0 and is abandoned
+    if (t < 0 || t >= p.V) raise_error(p, kErrBadToken);  // the step decodes token 0 and is abandoned
   }
   uint64_t* trace = p.trace ? p.trace + static_cast<size_t>(blockIdx.x) * p.trace_stride : nullptr;
   int ev = 0;
@@ -1490,21 +1433,20 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   };
 
   gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv, p.s_qkv, H, qkv_pairs, false, R);
-  rmsnorm_embed_to_lds<FMT>(p, p.norm_in, xs, red);
+  rmsnorm_embed_to_lds<FMT>(p, p.norm_in, xs, red, dump_at(p, 0, kDH));
   stamp();
   wg_barrier();
   for (int l = 0; l < L; ++l) {
     if (l > 0) {  // RMSNorm of the residual written by the previous layer's down stage
-      ok = norm_from_x<FMT>(p, p.norm_in + static_cast<size_t>(l) * H, tag_of(p, l - 1, kTagXD), xs, red);
+      ok = norm_from_x<FMT>(p, p.norm_in + static_cast<size_t>(l) * H, tag_of(p, l - 1, kTagXD), xs, red,
+                           dump_at(p, l, kDH));
       stamp();
       if (!handoff_done()) return;
     }
     // QKV GEMV -> RoPE; q, K/V(pos) as tagged words, K/V(pos) also into the cache
     gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
-                           tag_of(p, l, kTagQKV));
-    fstamp(p, l, 5);
+                           tag_of(p, l, kTagQKV), dump_at(p, l, kDQKV));
     attention_prefetch<HD, GMAX>(p, l, AR);
-    fstamp(p, l, 6);
     wg_barrier();  // every wave is done with xs
     stamp();
     ok = poll_q_kv<HD>(p, l, qs);
@@ -1518,28 +1460,25 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     stamp();
     gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, l == 0, R);
     wg_barrier();  // attention is done with LDS
-    if (ok) ok = vector_from_words<FMT>(p, p.to, qdim, tag_of(p, l, kTagO), xs);
+    if (ok) ok = vector_from_words<FMT>(p, p.to, qdim, tag_of(p, l, kTagO), xs, dump_at(p, l, kDO));
     stamp();
     if (!handoff_done()) return;
 
     // O-projection + residual
     gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, xs, l, l == 0, R,
-                             tag_of(p, l, kTagXO));
-    fstamp(p, l, 7);
+                             tag_of(p, l, kTagXO), dump_at(p, l, kDWO));
     gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, false, R);
-    fstamp(p, l, 8);
     wg_barrier();
     stamp();
-    ok = norm_from_x<FMT>(p, p.norm_post + static_cast<size_t>(l) * H, tag_of(p, l, kTagXO), xs, red);
+    ok = norm_from_x<FMT>(p, p.norm_post + static_cast<size_t>(l) * H, tag_of(p, l, kTagXO), xs, red,
+                         dump_at(p, l, kDH2));
     stamp();
     if (!handoff_done()) return;
 
     // gate/up GEMV -> SwiGLU
     gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, xs, l, false, R,
-                              tag_of(p, l, kTagM));
-    fstamp(p, l, 9);
+                              tag_of(p, l, kTagM), dump_at(p, l, kDGU));
     gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
-    fstamp(p, l, 10);
     wg_barrier();
     stamp();
     ok = vector_from_words16<FMT>(p, reinterpret_cast<const uint32_t*>(p.tm), p.F, tag_of(p, l, kTagM), xs);
@@ -1548,8 +1487,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
 
     // down GEMV + residual
     gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, xs, l, false, R,
-                             tag_of(p, l, kTagXD));
-    fstamp(p, l, 11);
+                             tag_of(p, l, kTagXD), dump_at(p, l, kDWD));
     if (l + 1 < L)
       gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);
@@ -1562,25 +1500,15 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   }
   // final RMSNorm -> lm_head (in the lm_head's own storage format, which sets the LDS layout)
   const bool head16 = FMT != 0 && p.lm_fmt == 0;
-  if (head16) ok = norm_from_x<0>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
-  else ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red);
+  if (head16) ok = norm_from_x<0>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red, dump_at(p, L, kDH));
+  else ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red, dump_at(p, L, kDH));
   stamp();
   if (!handoff_done()) return;
-  const EpiState st = head16 ? gemv_run<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u)
-                             : gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u);
+  const EpiState st = head16 ? gemv_run<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr)
+                             : gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr);
   wg_barrier();
   stamp();
   if (p.next_token != nullptr) greedy_token(p, st, smem, red, ired);
-}
-
-// barrier microbenchmark: `iters` grid barriers in one persistent launch
-__global__ void __launch_bounds__(kThreads, 1) amk_barrier_kernel(unsigned* ctr, unsigned* err, int iters) {
-  __shared__ int abort_flag;
-  if (threadIdx.x == 0) abort_flag = 0;
-  __syncthreads();
-  GridBarrier bar{ctr, 0u, 0u, 100000000ull, err, nullptr, 0};
-  for (int i = 0; i < iters; ++i)
-    if (!bar.sync(&abort_flag)) return;
 }
 
 template __global__ void amk_decode_kernel<64, 0, 4>(const KParams);
@@ -1595,6 +1523,14 @@ template __global__ void amk_decode_kernel<64, 2, 4>(const KParams);
 template __global__ void amk_decode_kernel<128, 2, 4>(const KParams);
 template __global__ void amk_decode_kernel<64, 2, 8>(const KParams);
 template __global__ void amk_decode_kernel<128, 2, 8>(const KParams);
+
+// Zeroes n 32-bit words (a model's scratch: error flag and exchange words) before the model is
+// used again after a failure; a kernel rather than a memset so that it is safe in graph capture.
+__global__ void amk_clear_kernel(uint32_t* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
 
 }  // namespace amk
 
@@ -1614,4 +1550,7 @@ extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(i
   if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 2) return nullptr;
   return t[head_dim == 128][gmax == 8][fmt];
 }
-extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle() { return (const void*)&amk::amk_barrier_kernel; }
+
+extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle() {
+  return (const void*)&amk::amk_clear_kernel;
+}

@@ -16,8 +16,7 @@
 #include "amk_kparams.h"
 
 extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax);
-extern "C" __attribute__((visibility("hidden"))) const void* amk_stream_kernel_handle(int head_dim, int fmt, int gmax);
-extern "C" __attribute__((visibility("hidden"))) const void* amk_barrier_kernel_handle();
+extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle();
 
 namespace {
 
@@ -96,8 +95,7 @@ struct amk_model {
   int lds_bytes = 0;
   int gmax = 4;
   int s_cap = 1;
-  bool stream = false;      // true: block-split kernel (amk_stream.hip); false: wave-row kernel
-  uint32_t tag0 = 1;        // tag base of the next launch (streaming kernel)
+  uint32_t tag0 = 1;        // tag base of the next launch
   const void* kernel = nullptr;
   uint64_t spin_limit = kDefaultSpinLimit;
   uint64_t* trace = nullptr;
@@ -107,6 +105,9 @@ struct amk_model {
   size_t weight_bytes = 0;
   uint8_t* scratch = nullptr;
   size_t scratch_bytes = 0;
+  unsigned* herr = nullptr;  // pinned host word the first failing block of a launch writes its code to
+  float* dump = nullptr;     // per-stage dump (amk_set_dump), or null
+  int64_t dump_layer = 0;    // floats per layer of the dump
   amk::KParams kp{};  // pointers and dims filled at load; step fields filled per call
   // packing metadata for export
   size_t off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0, off_lm = 0;
@@ -138,6 +139,34 @@ int validate_config(const amk_config* c) {
         c->rope_original_ctx > 0))
     return fail(AMK_ERR_UNSUPPORTED, "rope scaling parameters");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(AMK_ERR_UNSUPPORTED, "rms_eps / rope_theta");
+  // the kernel addresses every packed matrix, the embedding and each (layer, K/V, kv head) block
+  // of the cache through buffer resources with 32-bit byte offsets
+  const int64_t H = c->hidden, F = c->ffn, V = c->vocab, hd = c->head_dim;
+  const int64_t QD = c->n_q_heads * hd, QKV = QD + 2 * c->n_kv_heads * hd;
+  const int64_t pbits = c->weight_format == AMK_BF16 ? 16 : (c->weight_format == AMK_W4A16 ? 4 : 8);
+  const int64_t lm_bits = c->weight_format == AMK_W8A16 ? 8 : 16;
+  const int64_t lim = int64_t(1) << 31;
+  if (QKV * H * pbits / 8 >= lim || H * QD * pbits / 8 >= lim || 2 * F * H * pbits / 8 >= lim ||
+      H * F * pbits / 8 >= lim || V * H * lm_bits / 8 >= lim || V * H * 2 >= lim ||
+      static_cast<int64_t>(c->max_ctx) * hd * 2 >= lim)
+    return fail(AMK_ERR_UNSUPPORTED, "a weight matrix, the embedding or a KV-cache block reaches 2^31 bytes");
+  return AMK_OK;
+}
+
+// Conditions on the grid (one persistent block per compute unit) that the tagged hand-offs rely
+// on. An exchange word is overwritten by the next stage of the same kind, one layer later; every
+// block that polls it must have finished before that. A block's stages run in order, so it holds
+// up the overwriting stage if it produces some value on the way to it: with the strided row map
+// block b owns row pair b of every GEMV stage, so fewer pairs than blocks in the gate/up stage
+// (between the x-after-O poll and the down stage that rewrites x) or, with two or more layers, in
+// the QKV stage (between the x-after-down poll and the next O stage) would let a block without
+// rows fall behind. Attention units are one per block, so nkv cannot exceed the grid.
+int validate_grid(const amk_config& c, int grid) {
+  const int64_t qkv_pairs = static_cast<int64_t>(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim / 2;
+  if (c.n_kv_heads > grid) return fail(AMK_ERR_UNSUPPORTED, "n_kv_heads exceeds the number of compute units");
+  if (c.ffn < grid) return fail(AMK_ERR_UNSUPPORTED, "ffn below the number of compute units");
+  if (c.n_layers >= 2 && qkv_pairs < grid)
+    return fail(AMK_ERR_UNSUPPORTED, "(n_q_heads + 2 n_kv_heads) * head_dim / 2 below the number of compute units");
   return AMK_OK;
 }
 
@@ -205,6 +234,13 @@ const char* amk_status_string(int status) {
   s = base;
   if (status != AMK_OK && !g_last_error.empty()) s += ": " + g_last_error;
   return s.c_str();
+}
+
+int amk_validate_config(const amk_config* cfg, int32_t compute_units) {
+  const int st = validate_config(cfg);
+  if (st) return st;
+  if (compute_units <= 0) return fail(AMK_ERR_INVALID_ARG, "compute_units must be positive");
+  return validate_grid(*cfg, compute_units);
 }
 
 int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes, float* scales) {
@@ -278,42 +314,17 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
 
   // grid / LDS / splits
   m->grid = prop.multiProcessorCount;
+  st = validate_grid(c, m->grid);
+  if (st) { delete m; return st; }
   const int G = c.n_q_heads / c.n_kv_heads;
   m->gmax = G <= 4 ? 4 : 8;
-  {
-    const char* kv = std::getenv("AMK_KERNEL");
-    m->stream = kv && std::string(kv) == "block" && (c.weight_format == AMK_BF16 || c.weight_format == AMK_W8A16);
-  }
-  if (m->stream && m->gmax != 4) m->stream = false;  // the block-split kernel covers G <= 4
-  // split cap: one attention unit per block; the streaming kernel's split merge puts the splits
-  // of one output on the lanes of a wave, so it takes at most 64
+  // split cap: one attention unit per block, and the split merge puts the splits of one output
+  // on the lanes of a wave, so at most 64
   m->s_cap = std::min(64, std::max(1, m->grid / c.n_kv_heads));
   const int cw = 8192 / pbits;  // columns per 1 KB weight chunk
   auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
-  auto a4 = [](int64_t n) { return (n + 3) / 4 * 4; };
   const int64_t xs_f = std::max({pad(H), pad(QD), pad(F)});
-  if (m->stream) {
-    const int64_t nb = m->grid;
-    auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
-    const int64_t qkv_pairs = QKV / 2;
-    const int64_t maxpairs = std::max({cdiv(qkv_pairs, nb), cdiv(H / 2, nb), 2 * cdiv(F / 2, nb), cdiv(V / 2, nb)});
-    const int64_t waves = amk::kWaves;
-    const int64_t vec = a4(std::max(xs_f, G * hd + hd));
-    const int64_t part = a4(std::max(maxpairs * waves * 2, waves * G * (hd + 2)));
-    const int64_t scl_stride = a4(2 * maxpairs);
-    const int64_t xres = a4(2 * cdiv(H / 2, nb)), rope = a4(hd);
-    if (maxpairs > amk::kThreads) { delete m; return fail(AMK_ERR_UNSUPPORTED, "too many row pairs per block"); }
-    if (H > 8192 || F > 32768) { delete m; return fail(AMK_ERR_UNSUPPORTED, "hidden or ffn too large"); }
-    int64_t o = vec;
-    m->kp.lds_part = static_cast<int32_t>(o); o += part;
-    m->kp.lds_scl = static_cast<int32_t>(o); m->kp.lds_scl_stride = static_cast<int32_t>(scl_stride); o += 2 * scl_stride;
-    m->kp.lds_nw = 0;
-    m->kp.lds_xres = static_cast<int32_t>(o); o += xres;
-    m->kp.lds_rope = static_cast<int32_t>(o); o += rope;
-    if (V / 2 * nb >= (int64_t(1) << 31)) { delete m; return fail(AMK_ERR_UNSUPPORTED, "vocab too large for the block split"); }
-    m->lds_bytes = static_cast<int>(4 * o);
-    m->kernel = amk_stream_kernel_handle(static_cast<int>(hd), q8 ? 1 : 0, m->gmax);
-  } else {
+  {
     // attention: every row's softmax state (a row: the lanes holding one position of a wave's
     // load, 512 / hd rows per wave), each head's max and sum, then q of the G heads and K/V(pos)
     const int64_t rows = static_cast<int64_t>(amk::kWaves) * (512 / hd);
@@ -352,6 +363,15 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_OOM, std::string("hipMalloc(scratch): ") + hipGetErrorString(he)); }
   he = hipMemset(m->scratch, 0, m->scratch_bytes);
   if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_HIP, std::string("hipMemset: ") + hipGetErrorString(he)); }
+  // coherent pinned host memory: a system-scope store from the kernel is visible to the host
+  // without a synchronisation
+  he = hipHostMalloc(reinterpret_cast<void**>(&m->herr), 64, hipHostMallocMapped | hipHostMallocCoherent);
+  if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(he)); }
+  __atomic_store_n(m->herr, 0u, __ATOMIC_RELEASE);
+  unsigned* herr_dev = nullptr;
+  he = hipHostGetDevicePointer(reinterpret_cast<void**>(&herr_dev), m->herr, 0);
+  if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_HIP, std::string("hipHostGetDevicePointer: ") + hipGetErrorString(he)); }
+  m->dump_layer = 6 * H + QKV + 2 * QD + 3 * F;  // the slots of one layer in the dump
 
   // ---------------- packing + upload ----------------
   std::vector<uint8_t> stage;
@@ -504,6 +524,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   uint8_t* S = m->scratch;
   k.s_cap = m->s_cap;
   k.err = reinterpret_cast<unsigned*>(S + s_err);
+  k.herr = herr_dev;
   k.spin_limit = m->spin_limit;
   k.tagged = reinterpret_cast<uint64_t*>(S + s_tag);
   k.tagged_bytes = static_cast<uint32_t>(s_tag_end - s_tag);
@@ -519,10 +540,43 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
 }
 
 namespace {
+// Enqueues on `stream` the reset of the model's device state after a failed step: the error flag
+// and every exchange word go back to zero (after every launch already enqueued), and the tags
+// restart at 1, above the zero of a cleared word.
+int enqueue_reset(amk_model* m, void* stream) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(m->scratch);
+  size_t n = m->scratch_bytes / 4;
+  void* args[] = {&p, &n};
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>(1024, (n + 255) / 256));
+  HIP_TRY(hipLaunchKernel(amk_clear_kernel_handle(), dim3(blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
+  m->tag0 = 1;
+  return AMK_OK;
+}
+
+// Error code of a device failure as an ABI status (with its description).
+int device_error_status(unsigned code) {
+  if (code == amk::kErrBadToken) return fail(AMK_ERR_INVALID_ARG, "a greedy step read a device token outside [0, vocab)");
+  return fail(AMK_ERR_SYNC_TIMEOUT, "a decode step abandoned a hand-off wait (bounded poll timed out)");
+}
+
+// A failure of an earlier step that the device has already reported through the pinned host word
+// (read without synchronising): clears the word, enqueues the reset, and returns the error;
+// AMK_OK when there is none. Exactly one block of a failed launch writes the word.
+int take_pending_error(amk_model* m, void* stream) {
+  const unsigned code = __atomic_load_n(m->herr, __ATOMIC_ACQUIRE);
+  if (code == 0u) return AMK_OK;
+  __atomic_store_n(m->herr, 0u, __ATOMIC_RELEASE);
+  const int rc = enqueue_reset(m, stream);
+  if (rc) return rc;
+  return device_error_status(code);
+}
+
 // One decode step: a single cooperative launch. token_dev / next_token are null for a
-// host-token step.
+// host-token step. A pending failure of an earlier step is reported instead of launching.
 int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t pos, void* kv_cache,
                 float* logits_out, int32_t* next_token, void* stream) {
+  const int pending = take_pending_error(m, stream);
+  if (pending) return pending;
   amk::KParams k = m->kp;
   k.token = token;
   k.token_dev = token_dev;
@@ -535,7 +589,7 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   // the attention output itself, with no merge hand-off.
   const int tstep = amk::kWaves * (m->gmax > 4 ? 2 : 4) * (512 / m->cfg.head_dim);
   int T = std::max(16, (ctx + m->s_cap - 1) / m->s_cap);
-  if (!m->stream && ctx <= tstep) T = tstep;
+  if (ctx <= tstep) T = tstep;
   k.T = T;
   k.S = (ctx + T - 1) / T;
   k.kv = static_cast<uint16_t*>(kv_cache);
@@ -543,6 +597,8 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   k.spin_limit = m->spin_limit;
   k.trace = m->trace;
   k.trace_stride = m->trace_stride;
+  k.dump = m->dump;
+  k.dump_stride = m->dump_layer;
   k.tag0 = m->tag0;
   m->tag0 += static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
   void* args[] = {&k};
@@ -563,25 +619,28 @@ int amk_decode_step_greedy(amk_model* m, const int32_t* token_in, int32_t pos, v
                            int32_t* next_token_out, void* stream) {
   if (!m || !token_in || !kv_cache || !next_token_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
   if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
-  if (m->stream) return fail(AMK_ERR_UNSUPPORTED, "greedy steps run on the wave-row kernel only");
   return launch_step(m, 0, token_in, pos, kv_cache, logits_out, next_token_out, stream);
 }
 
 int amk_sync(amk_model* m, void* stream) {
   if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  unsigned err = 0;
-  HIP_TRY(hipMemcpy(&err, m->kp.err, 4, hipMemcpyDeviceToHost));
-  if (err != 0) {
-    // words the abandoned step left carry older tags than any later step polls for: only the
-    // flag needs clearing
-    HIP_TRY(hipMemset(m->kp.err, 0, 4));
-    HIP_TRY(hipDeviceSynchronize());
-    if (err == amk::kErrBadToken)
-      return fail(AMK_ERR_INVALID_ARG, "a greedy step read a device token outside [0, vocab)");
-    return fail(AMK_ERR_SYNC_TIMEOUT, "a decode step abandoned a hand-off wait");
+  int rc = take_pending_error(m, stream);
+  if (rc == AMK_OK) {
+    // the device flag is the authority; the host word only saves the call a synchronisation
+    unsigned err = 0;
+    HIP_TRY(hipMemcpy(&err, m->kp.err, 4, hipMemcpyDeviceToHost));
+    if (err != 0u) {
+      const int r = enqueue_reset(m, stream);
+      rc = r ? r : device_error_status(err);
+    }
   }
-  return AMK_OK;
+  if (rc != AMK_OK) {
+    const std::string keep = g_last_error;
+    HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));  // the reset has run
+    g_last_error = keep;
+  }
+  return rc;
 }
 
 size_t amk_kv_cache_bytes(const amk_model* m) {
@@ -603,7 +662,8 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   info->scratch_bytes = static_cast<int64_t>(m->scratch_bytes);
   info->max_splits = m->s_cap;
   info->device = m->device;
-  info->kernel = m->stream ? AMK_KERNEL_BLOCK : AMK_KERNEL_WAVE;
+  info->dump_layer_floats = m->dump_layer;
+  info->dump_floats = m->dump_layer * m->cfg.n_layers + m->cfg.hidden;
   return AMK_OK;
 }
 
@@ -663,43 +723,6 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
   return AMK_OK;
 }
 
-int amk_bench_barrier(int32_t iters, float* us_out) {
-  if (iters <= 0 || !us_out) return fail(AMK_ERR_INVALID_ARG, "iters <= 0 or null out");
-  int dev = 0;
-  HIP_TRY(hipGetDevice(&dev));
-  hipDeviceProp_t prop;
-  HIP_TRY(hipGetDeviceProperties(&prop, dev));
-  unsigned* buf = nullptr;
-  HIP_TRY(hipMalloc(&buf, 4 * amk::kCtrStride * (amk::kBarrierCtrs + 1)));
-  int rc = AMK_OK;
-  hipEvent_t a = nullptr, b = nullptr;
-  do {
-    hipError_t e = hipMemset(buf, 0, 4 * amk::kCtrStride * (amk::kBarrierCtrs + 1));
-    if (e == hipSuccess) e = hipEventCreate(&a);
-    if (e == hipSuccess) e = hipEventCreate(&b);
-    unsigned* ctr = buf;
-    unsigned* err = buf + amk::kCtrStride * amk::kBarrierCtrs;
-    void* args[] = {&ctr, &err, &iters};
-    if (e == hipSuccess) e = hipEventRecord(a, nullptr);
-    if (e == hipSuccess)
-      e = hipLaunchCooperativeKernel(amk_barrier_kernel_handle(), dim3(prop.multiProcessorCount), dim3(amk::kThreads),
-                                     args, 0, nullptr);
-    if (e == hipSuccess) e = hipEventRecord(b, nullptr);
-    if (e == hipSuccess) e = hipEventSynchronize(b);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
-    unsigned herr = 0;
-    if (e == hipSuccess) e = hipMemcpy(&herr, err, 4, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) { rc = fail(AMK_ERR_HIP, std::string("barrier bench: ") + hipGetErrorString(e)); break; }
-    if (herr) { rc = fail(AMK_ERR_SYNC_TIMEOUT, "barrier bench timed out"); break; }
-    *us_out = ms * 1000.f / static_cast<float>(iters);
-  } while (false);
-  if (a) hipEventDestroy(a);
-  if (b) hipEventDestroy(b);
-  hipFree(buf);
-  return rc;
-}
-
 int amk_set_spin_limit(amk_model* m, uint64_t ticks) {
   if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
   m->spin_limit = ticks ? ticks : kDefaultSpinLimit;
@@ -715,9 +738,18 @@ int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block) {
   return AMK_OK;
 }
 
+int amk_set_dump(amk_model* m, float* dump, int64_t floats) {
+  if (!m) return fail(AMK_ERR_INVALID_ARG, "null handle");
+  if (dump && floats < m->dump_layer * m->cfg.n_layers + m->cfg.hidden)
+    return fail(AMK_ERR_INVALID_ARG, "dump buffer too small");
+  m->dump = dump;
+  return AMK_OK;
+}
+
 int amk_free(amk_model* m) {
   if (!m) return AMK_OK;
   int rc = AMK_OK;
+  if (m->herr && hipHostFree(m->herr) != hipSuccess) rc = fail(AMK_ERR_HIP, "hipHostFree(error word)");
   if (m->weights && hipFree(m->weights) != hipSuccess) rc = fail(AMK_ERR_HIP, "hipFree(weights)");
   if (m->scratch && hipFree(m->scratch) != hipSuccess) rc = fail(AMK_ERR_HIP, "hipFree(scratch)");
   delete m;

@@ -6,14 +6,13 @@ namespace amk {
 
 constexpr int kThreads = 512;          // threads per persistent block (8 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line per counter
-constexpr int kBarrierCtrs = 8;        // arrival counters of the barrier microbenchmark
+constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line
 
 // Tags of the exchange words: stage `which` of layer l in a launch writes tag
 // tag0 + l * kTagsPerLayer + which; the host advances tag0 by kTagsPerLayer * L + 1 per launch.
 constexpr int kTagsPerLayer = 6;
 // device error flag values
-constexpr unsigned kErrTimeout = 1;   // a hand-off poll (or barrier wait) exceeded spin_limit
+constexpr unsigned kErrTimeout = 1;   // a hand-off poll exceeded spin_limit
 constexpr unsigned kErrBadToken = 2;  // a device-resident input token was outside [0, V)
 enum { kTagQKV = 0, kTagPart = 1, kTagO = 2, kTagXO = 3, kTagM = 4, kTagXD = 5 };
 
@@ -49,6 +48,7 @@ struct KParams {
   // scratch (library-owned)
   int32_t s_cap;                            // split capacity per kv head (partials stride)
   unsigned* err;                            // device error flag
+  unsigned* herr;                           // pinned host word: the code of the error that set err
   uint64_t spin_limit;                      // wall-clock ticks per hand-off poll
   // tagged exchange words (low 32 bits payload, high 32 bits tag), all inside one region so a
   // single buffer resource covers them
@@ -60,12 +60,11 @@ struct KParams {
   uint64_t* to;                             // [nq*hd/2] attention output, 2 bf16 per word
   uint64_t* targ;                           // [grid][2] greedy step: each block's argmax (value, index)
   uint64_t* tm;                             // SwiGLU output: [F] 32-bit words bf16 << 16 | tag & 0xffff
-                                            // (wave-row kernel) or [F/2] 2 bf16 per word (block kernel)
   uint32_t tag0;
-  // block-split kernel: LDS layout (offsets in floats)
-  int32_t lds_part, lds_scl, lds_scl_stride, lds_nw, lds_xres, lds_rope;
   uint64_t* trace;                          // optional [grid][trace_stride] wall-clock stamps
   int32_t trace_stride;
+  float* dump;                              // optional per-stage dump, dump_stride floats per layer
+  int64_t dump_stride;
 };
 
 }  // namespace amk

@@ -78,17 +78,6 @@ typedef struct {
 
 typedef struct amk_model amk_model; /* opaque, library-owned */
 
-/* Kernel a model runs. Both are one persistent cooperative launch per token with the same
- * tagged hand-offs between stages; they differ in how a block splits a GEMV stage:
- *   AMK_KERNEL_WAVE  (default): every wave owns whole output-row pairs and finishes them on its
- *                    own (register window per wave, per-wave epilogue);
- *   AMK_KERNEL_BLOCK: a block's 8 waves split the K axis of the block's rows (register weight
- *                    ring, block-wide epilogue through LDS); only for models with at most 4
- *                    query heads per kv head, selected with the environment variable
- *                    AMK_KERNEL=block at load time. */
-#define AMK_KERNEL_WAVE 0
-#define AMK_KERNEL_BLOCK 1
-
 /* Launch geometry and memory of a loaded model (for tests and benchmarks). */
 typedef struct {
   int32_t grid_blocks;          /* persistent blocks (one per compute unit)                 */
@@ -100,7 +89,8 @@ typedef struct {
   int64_t scratch_bytes;        /* device bytes of library scratch                           */
   int32_t max_splits;           /* upper bound on KV splits per kv head                      */
   int32_t device;               /* HIP device the model lives on                             */
-  int32_t kernel;               /* AMK_KERNEL_WAVE or AMK_KERNEL_BLOCK                       */
+  int64_t dump_layer_floats;    /* floats per layer of the per-stage dump (amk_set_dump)      */
+  int64_t dump_floats;          /* floats of a whole dump: n_layers * dump_layer_floats + H  */
 } amk_info;
 
 /* Copies, packs, (for the W8A16 formats) quantizes and uploads a model to the current device.
@@ -126,12 +116,27 @@ typedef struct {
  * |q| of column k + 4 in bits 4..6, and the sign of column (k + 3) mod 4 + 4 in bit 3.
  * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
  * *out receives a model handle owned by the library until amk_free.
- * Errors: INVALID_ARG (null pointers, wrong n_tensors), UNSUPPORTED (shape checks: head_dim
- * in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd multiples of 16, or of 32
- * for AMK_W4A16, vocab and hidden even, max_ctx >= 1), HIP, OOM, COOPERATIVE (no co-resident
- * persistent grid). */
+ * Errors: INVALID_ARG (null pointers, wrong n_tensors); UNSUPPORTED for a shape outside the
+ * supported set: head_dim in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd
+ * multiples of 16 (of 32 for AMK_W4A16), vocab even, hidden <= 8192, ffn and nq*hd <= 32768,
+ * every packed weight matrix, the embedding and each (layer, K/V, kv head) block of the cache
+ * below 2^31 bytes (the kernel addresses them with 32-bit offsets); and, on the current device
+ * with G compute units (one persistent block each): nkv <= G, ffn >= G, and for n_layers >= 2
+ * (nq + 2 nkv) * head_dim / 2 >= G. The last two give every block at least one row pair of the
+ * gate/up and QKV stages, which the tagged hand-offs need: a block then cannot fall a whole
+ * layer behind the blocks that overwrite the exchange words it still polls. HIP, OOM,
+ * COOPERATIVE (no co-resident persistent grid). */
 int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_tensors,
                      int32_t n_tensors, amk_model** out);
+
+/* Checks a model description against everything amk_load_weights requires of it, for a device
+ * with `compute_units` compute units (the persistent grid has one block per unit; MI355X: 256),
+ * on the host only: no GPU is needed and nothing is allocated. The pages validate a schedule
+ * before it reaches the GPU, so a bad one gets a clean rejection instead of a hang (gist.science
+ * explainer, Methodology > Safety Gate); here the schedule is fixed, and what can be rejected is
+ * the model shape. Returns AMK_OK, or UNSUPPORTED with the reason in amk_status_string (the
+ * conditions are listed at amk_load_weights); INVALID_ARG for a null cfg or compute_units <= 0. */
+int amk_validate_config(const amk_config* cfg, int32_t compute_units);
 
 /* Decodes one token: feeds `token` at position `pos`, writes K/V of position `pos` in every
  * layer of `kv_cache`, attends over positions [0, pos] inclusive, and writes fp32 logits.
@@ -140,9 +145,22 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* host_bf16_ten
  * kv_cache: device bf16 [L][2 (K, V)][nkv][max_ctx][head_dim], amk_kv_cache_bytes() long,
  *   caller-owned; slots [0, pos) must already hold this sequence's keys/values.
  * logits_out: device fp32 [V], caller-owned.
- * Errors (checked on the host before any HIP call): INVALID_ARG for null handle/pointers,
- * token outside [0, V) or pos outside [0, max_ctx); HIP if the launch fails. A hand-off
- * timeout of an earlier step is reported as SYNC_TIMEOUT by amk_sync.
+ * Errors:
+ *   - INVALID_ARG for a null handle or pointer, token outside [0, V) or pos outside
+ *     [0, max_ctx): checked on the host before any HIP call;
+ *   - SYNC_TIMEOUT or INVALID_ARG for a failure of an EARLIER step of this model that has
+ *     completed on the device by the time of this call: a hand-off wait that exceeded its bound
+ *     (SYNC_TIMEOUT), or an out-of-range device token of a greedy step (INVALID_ARG). The kernel
+ *     raising the error writes its code to a word in pinned host memory, which this call reads
+ *     without synchronising. The call then launches nothing: it enqueues, on `stream`, the reset
+ *     of the model's device state (exchange words and error flag), after which the model is
+ *     usable again, and returns the error. The failed step's outputs are undefined (it may have
+ *     written some, all or none of its logits, K/V slots and token); steps launched after it
+ *     and before the reset did nothing: their logits_out and K/V slots are left unwritten. A
+ *     failure whose kernel has not finished yet is reported by a later call or by amk_sync.
+ *     The pages require a clean rejection instead of a hung GPU (gist.science explainer,
+ *     Methodology > Safety Gate): every wait in the kernel is bounded;
+ *   - HIP if the launch fails.
  * Concurrency: one handle must not run two steps at once (they share the scratch). */
 int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
                     float* logits_out, void* stream);
@@ -159,16 +177,18 @@ int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
  * logits_out: device fp32 [V] or NULL (then no logits are written);
  * kv_cache, pos, stream: as for amk_decode_step. All buffers are caller-owned.
  * Errors: INVALID_ARG for a null handle, token_in, kv_cache or next_token_out, or pos outside
- * [0, max_ctx) (host checks, before any HIP call); UNSUPPORTED if the model runs the block-split
- * kernel; HIP if the launch fails. A token_in value outside [0, V) cannot be checked on the host:
- * the step then decodes token 0, is abandoned, and amk_sync reports INVALID_ARG. */
+ * [0, max_ctx) (host checks, before any HIP call); an earlier step's failure as for
+ * amk_decode_step; HIP if the launch fails. A token_in value outside [0, V) cannot be checked
+ * on the host: the step then decodes token 0 in its place, its outputs are undefined, and the
+ * next call (or amk_sync) reports INVALID_ARG. */
 int amk_decode_step_greedy(amk_model* m, const int32_t* token_in, int32_t pos, void* kv_cache,
                            float* logits_out, int32_t* next_token_out, void* stream);
 
-/* Waits for `stream` and reports a device-side error raised by earlier steps of this model
- * (AMK_ERR_SYNC_TIMEOUT for an abandoned hand-off wait, AMK_ERR_INVALID_ARG for an out-of-range
- * device token of a greedy step), then clears it so the model is usable again. Steps launched
- * after the error and before amk_sync do nothing. */
+/* Waits for `stream` and reports a device-side error raised by an earlier step of this model
+ * that no step call has reported yet (AMK_ERR_SYNC_TIMEOUT for an abandoned hand-off wait,
+ * AMK_ERR_INVALID_ARG for an out-of-range device token of a greedy step), then resets the
+ * model's device state and waits for the reset, so the model is usable again. Steps launched
+ * after the error and before the reset do nothing (their outputs are left unwritten). */
 int amk_sync(amk_model* m, void* stream);
 
 /* Bytes of the caller-owned KV cache: L * 2 * nkv * max_ctx * head_dim * 2. 0 for NULL. */
@@ -207,11 +227,6 @@ int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* cod
 int amk_quantize_int4(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
                       float* scales);
 
-/* Measures a classic grid barrier (arrival counters + polling, the pattern the tagged hand-offs
- * replace) for reference: runs `iters` barriers in one persistent launch on the current device
- * and stores the mean microseconds per barrier in *us_out. Synchronous. */
-int amk_bench_barrier(int32_t iters, float* us_out);
-
 /* Debug control: bound (in 100 MHz wall-clock ticks) on any single hand-off poll or barrier
  * wait; 0 restores the default (one second). A tiny bound makes steps fail cleanly with
  * SYNC_TIMEOUT, which is how the timeout path is exercised. */
@@ -227,6 +242,30 @@ int amk_set_spin_limit(amk_model* m, uint64_t ticks);
  * trace: device uint64 [grid_blocks][events_per_block], caller-owned. NULL switches tracing off.
  * Errors: INVALID_ARG for a null handle or a too small events_per_block. */
 int amk_set_trace(amk_model* m, uint64_t* trace, int32_t events_per_block);
+
+/* Debug control: per-stage dumps, so each stage of every layer can be checked against the plain
+ * definition applied to the kernel's own input for that stage (the pages check the generated
+ * kernel's parts in isolation against eager references: gist.science explainer, Methodology >
+ * Layer 1). When dump is non-NULL, every later step of this model writes fp32 values into it:
+ * for layer l, at dump + l * S (S = amk_info.dump_layer_floats = 6 H + QKV + 2 QD + 3 F with
+ * QKV = (nq + 2 nkv) head_dim and QD = nq head_dim), in this order:
+ *   h [H]        RMSNorm output that feeds the QKV projection (bf16 values);
+ *   qkv [QKV]    QKV projection output before RoPE (row scale applied), q | k | v rows in the
+ *                canonical order of q_proj, k_proj, v_proj;
+ *   q [QD]       q after RoPE;
+ *   o [QD]       attention output (bf16 values), head-major;
+ *   wo [H]       O-projection output;
+ *   x_o [H]      residual after the O-projection;
+ *   h2 [H]       RMSNorm output that feeds gate/up (bf16 values);
+ *   gu [2F]      gate outputs [F], then up outputs [F];
+ *   m [F]        SwiGLU output (bf16 values);
+ *   wd [H]       down-projection output;
+ *   x_d [H]      residual after the down projection;
+ * then, at dump + L * S, the final RMSNorm output [H] that feeds the lm_head. The K/V of the
+ * step's position are in the KV cache and the logits in logits_out. dump: device fp32 of at
+ * least floats = amk_info.dump_floats elements, caller-owned. NULL switches dumping off.
+ * Errors: INVALID_ARG for a null handle or floats too small. */
+int amk_set_dump(amk_model* m, float* dump, int64_t floats);
 
 /* Releases every device and host resource of the handle. NULL is accepted. */
 int amk_free(amk_model* m);

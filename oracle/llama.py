@@ -132,12 +132,16 @@ class Linear:
 
     BLOCK = 8192
 
-    def __init__(self, bits: np.ndarray, fmt: int, widen_once: bool):
+    def __init__(self, bits: np.ndarray, fmt: int, widen_once: bool, widen64: bool = False):
+        """widen_once keeps the weights (codes or bf16 values) widened to float32 for the life of
+        the object instead of widening one row block per call; widen64 also keeps a float64 copy
+        for the float64-accumulation variant. Both only trade memory for time: the values are the
+        same exact integers or bf16 values either way."""
         bits = np.asarray(bits, dtype=np.uint16)
         self.rows, self.cols = bits.shape
         self.fmt = fmt
         self.codes = self.scales = self.bits = None
-        self._f32 = None
+        self._f32 = self._f64 = None
         if fmt in (FMT_W8A16, FMT_W4A16):
             quantize = quantize_rows_int8 if fmt == FMT_W8A16 else quantize_rows_int4
             self.codes, self.scales = quantize(bits)
@@ -147,8 +151,12 @@ class Linear:
             self.bits = bits
             if widen_once:
                 self._f32 = bf16_bits_to_f32(bits)
+        if widen_once and widen64:
+            self._f64 = self._f32.astype(np.float64)
 
-    def _block(self, r0: int, r1: int) -> np.ndarray:
+    def _block(self, r0: int, r1: int, accum=F32) -> np.ndarray:
+        if accum is np.float64 and self._f64 is not None:
+            return self._f64[r0:r1]
         if self._f32 is not None:
             return self._f32[r0:r1]
         if self.codes is not None:
@@ -163,7 +171,7 @@ class Linear:
         xa = x.astype(accum)
         for r0 in range(0, self.rows, self.BLOCK):
             r1 = min(self.rows, r0 + self.BLOCK)
-            W = self._block(r0, r1).astype(accum, copy=False)
+            W = self._block(r0, r1, accum).astype(accum, copy=False)
             acc = xa @ W.T
             if self.codes is not None:
                 acc = acc * self.scales[r0:r1].astype(accum)
@@ -180,7 +188,7 @@ class OracleModel:
     """
 
     def __init__(self, shape, tensors: List[np.ndarray], weight_format: int,
-                 widen_once: Optional[bool] = None, threads: int = 1):
+                 widen_once: Optional[bool] = None, threads: int = 1, widen64: bool = False):
         self.shape = shape
         self.fmt = weight_format
         self.accum = F32  # float64 only to measure a workload's sensitivity to summation order
@@ -201,9 +209,9 @@ class OracleModel:
         if threads > 1:
             from concurrent.futures import ThreadPoolExecutor
             with ThreadPoolExecutor(threads) as ex:
-                lins = list(ex.map(lambda bf: Linear(bf[0], bf[1], widen_once), zip(mats, fmts)))
+                lins = list(ex.map(lambda bf: Linear(bf[0], bf[1], widen_once, widen64), zip(mats, fmts)))
         else:
-            lins = [Linear(b, f, widen_once) for b, f in zip(mats, fmts)]
+            lins = [Linear(b, f, widen_once, widen64) for b, f in zip(mats, fmts)]
         self.layers: List[Dict[str, object]] = []
         for l in range(L):
             t = tensors[1 + 9 * l: 1 + 9 * (l + 1)]
@@ -235,26 +243,36 @@ class OracleModel:
             q = W["q"].apply(h, A).reshape(nq, hd)
             k = W["k"].apply(h, A).reshape(nkv, hd)
             v = W["v"].apply(h, A).reshape(nkv, hd)
+            if trace is not None:
+                trace.setdefault("qkv", []).append(np.concatenate([q.reshape(-1), k.reshape(-1), v.reshape(-1)]))
             q = apply_rope(q, cos, sin)
             k = apply_rope(k, cos, sin)
             kv[l, 0, :, pos, :] = f32_to_bf16_bits(k)
             kv[l, 1, :, pos, :] = f32_to_bf16_bits(v)
             o = np.empty((nq, hd), dtype=F32)
-            for hq in range(nq):
-                g = hq // G
+            for g in range(nkv):  # q heads g*G .. g*G + G - 1 read kv head g
                 Kc = bf16_bits_to_f32(kv[l, 0, g, :pos + 1, :])
                 Vc = bf16_bits_to_f32(kv[l, 1, g, :pos + 1, :])
-                o[hq] = attention_head(q[hq], Kc, Vc, self.scale, A)
-            x = x + W["o"].apply(round_bf16(o.reshape(-1)), A)
+                for hq in range(g * G, (g + 1) * G):
+                    o[hq] = attention_head(q[hq], Kc, Vc, self.scale, A)
+            wo = W["o"].apply(round_bf16(o.reshape(-1)), A)
+            x = x + wo
+            xo = x
             h2 = round_bf16(rmsnorm(x, W["w_post"], s.rms_eps))
-            m = round_bf16(silu(W["gate"].apply(h2, A)) * W["up"].apply(h2, A))
-            x = x + W["down"].apply(m, A)
+            g, u = W["gate"].apply(h2, A), W["up"].apply(h2, A)
+            m = round_bf16(silu(g) * u)
+            wd = W["down"].apply(m, A)
+            x = x + wd
             if trace is not None:
                 trace.setdefault("h", []).append(h)
                 trace.setdefault("q", []).append(q.reshape(-1))
                 trace.setdefault("o", []).append(round_bf16(o.reshape(-1)))
+                trace.setdefault("wo", []).append(wo)
+                trace.setdefault("xo", []).append(xo.copy())
                 trace.setdefault("h2", []).append(h2)
+                trace.setdefault("gu", []).append(np.concatenate([g, u]))
                 trace.setdefault("m", []).append(m)
+                trace.setdefault("wd", []).append(wd)
                 trace.setdefault("x", []).append(x.copy())
         hf = round_bf16(rmsnorm(x, self.w_norm, s.rms_eps))
         if trace is not None:

@@ -106,8 +106,9 @@ def test_argument_validation_without_gpu():
     assert lib.amk_set_trace(None, None, 0) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_export_quantized(None, 1, None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_get_info(None, None) == A.AMK_ERR_INVALID_ARG
-    fs = ctypes.c_float()
-    assert lib.amk_bench_barrier(0, ctypes.byref(fs)) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_set_dump(None, None, 0) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_validate_config(None, 256) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_validate_config(ctypes.byref(cfg), 0) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_quantize_int8(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_quantize_int4(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
     # W4A16 rows must hold whole 16-byte lane loads: 32-column multiples
@@ -115,6 +116,52 @@ def test_argument_validation_without_gpu():
     bad.ffn = 1552
     assert lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h)) == A.AMK_ERR_UNSUPPORTED
     assert "invalid argument" in D.amk_status_string(A.AMK_ERR_INVALID_ARG)
+
+
+def _cfg(shape, fmt=D.AMK_W8A16, max_ctx=64):
+    return D.make_config(shape, max_ctx, fmt)
+
+
+def _rejected(cfg, cus=256):
+    st = A.lib().amk_validate_config(ctypes.byref(cfg), cus)
+    return st == A.AMK_ERR_UNSUPPORTED, D.amk_status_string(st) if st else "ok"
+
+
+def test_validate_config_measured_shapes_pass():
+    """Every measured workload's model loads on a 256-CU device (MI355X) in its format."""
+    for wl in W.WORKLOADS.values():
+        D.amk_validate_config(_cfg(wl.shape, wl.weight_format, wl.max_ctx + 1), 256)
+
+
+def test_validate_config_handoff_conditions():
+    """The grid conditions the tagged hand-offs need (one row pair of the QKV and gate/up stages
+    per block, one attention unit per kv head), checked on the host for a given CU count."""
+    # two layers whose QKV stage has 128 row pairs: blocks 128..255 would own none
+    small = W.ModelShape("l2-small-qkv", 256, 2, 2, 1, 64, 512, 512, True, 10000.0)
+    bad, why = _rejected(_cfg(small))
+    assert bad and "compute units" in why, why
+    # the same stage is fine on a 128-CU device, and with one layer (no later stage rewrites x)
+    D.amk_validate_config(_cfg(small), 128)
+    D.amk_validate_config(_cfg(W.ModelShape("l1-small-qkv", 256, 1, 2, 1, 64, 512, 512, True, 10000.0)), 256)
+    # gate/up with fewer row pairs than blocks
+    bad, why = _rejected(_cfg(W.ModelShape("small-ffn", 512, 2, 8, 2, 64, 240, 512, True, 10000.0)))
+    assert bad and "ffn" in why, why
+    # more kv heads than blocks (one attention unit per block)
+    assert _rejected(_cfg(W.ModelShape("kv-heavy", 4096, 1, 64, 64, 64, 4096, 512, True, 10000.0)), 32)[0]
+
+
+def test_validate_config_rejects_matrices_of_2gib():
+    """The kernel addresses each matrix, the embedding and each KV block with 32-bit offsets."""
+    big = W.ModelShape("wide-vocab", 8192, 2, 64, 8, 128, 28672, 131072, False, 500000.0)
+    for fmt in (D.AMK_BF16, D.AMK_W8A16_BF16_HEAD, D.AMK_W8A16):  # bf16 head / bf16 embedding: 2^31 bytes
+        bad, why = _rejected(_cfg(big, fmt))
+        assert bad and "2^31" in why, (fmt, why)
+    ok = W.ModelShape("wide-ok", 8192, 2, 64, 8, 128, 28672, 131070, False, 500000.0)
+    D.amk_validate_config(_cfg(ok, D.AMK_W8A16), 256)
+    # a (layer, K/V, kv head) cache block of 2^31 bytes
+    bad, why = _rejected(_cfg(W.LLAMA3_8B, D.AMK_W8A16, max_ctx=1 << 23))
+    assert bad and "2^31" in why, why
+    D.amk_validate_config(_cfg(W.LLAMA3_8B, D.AMK_W8A16, max_ctx=(1 << 23) - 1), 256)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -174,14 +174,30 @@ def test_greedy_chain_graph_replay():
 
 
 def test_greedy_bad_device_token_is_reported():
+    """Reported by amk_sync, or, once the failed step has completed, by the next step call (which
+    then launches nothing); either way the model is usable afterwards."""
     dec = D.Decoder(SHAPE, W.gen_weights(SHAPE, 15), D.AMK_W8A16, 16)
-    nxt = _tok(0)
+    nxt = _tok(-7)
     dec.step_greedy(_tok(SHAPE.vocab), 0, next_token_out=nxt)
     torch.cuda.synchronize()
     with pytest.raises(D.AmkError) as e:
         dec.sync()
     assert e.value.status == D.amk.AMK_ERR_INVALID_ARG
     dec.step_greedy(_tok(5), 0, next_token_out=nxt)
+    torch.cuda.synchronize()
+    dec.sync()
+    assert 0 <= int(nxt.item()) < SHAPE.vocab
+    # the next step call reports a completed failure without amk_sync, and launches nothing
+    dec.step_greedy(_tok(-1), 1, next_token_out=nxt)
+    torch.cuda.synchronize()
+    nxt.fill_(-7)
+    with pytest.raises(D.AmkError) as e:
+        dec.step_greedy(_tok(5), 1, next_token_out=nxt)
+    assert e.value.status == D.amk.AMK_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert int(nxt.item()) == -7
+    dec.sync()  # nothing left to report
+    dec.step_greedy(_tok(5), 1, next_token_out=nxt)
     torch.cuda.synchronize()
     dec.sync()
     assert 0 <= int(nxt.item()) < SHAPE.vocab
