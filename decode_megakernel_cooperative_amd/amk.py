@@ -28,7 +28,8 @@ AMK_W8A16 = 1
 AMK_W8A16_BF16_HEAD = 2
 AMK_W4A16 = 3
 
-EXPORTED = ("amk_validate_config", "amk_load_weights", "amk_decode_step", "amk_decode_step_greedy", "amk_sync",
+EXPORTED = ("amk_validate_config", "amk_load_weights", "amk_decode_step", "amk_decode_step_noalloc",
+            "amk_decode_step_greedy", "amk_sync",
             "amk_kv_cache_bytes", "amk_get_info", "amk_export_quantized", "amk_quantize_int8", "amk_quantize_int4",
             "amk_set_spin_limit", "amk_set_trace", "amk_set_dump", "amk_free", "amk_status_string")
 
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.amk_validate_config.argtypes = [ctypes.POINTER(amk_config), i32]
         L.amk_load_weights.argtypes = [ctypes.POINTER(amk_config), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]
         L.amk_decode_step.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.amk_decode_step_noalloc.argtypes = [vp, i32, i32, vp, vp, vp]
         L.amk_decode_step_greedy.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.amk_sync.argtypes = [vp, vp]
         L.amk_kv_cache_bytes.argtypes = [vp]
@@ -139,6 +141,12 @@ def amk_decode_step(model: int, token: int, pos: int, kv_cache, logits_out, stre
     kv = kv_cache.data_ptr() if hasattr(kv_cache, "data_ptr") else int(kv_cache or 0)
     lg = logits_out.data_ptr() if hasattr(logits_out, "data_ptr") else int(logits_out or 0)
     _check(lib().amk_decode_step(model, int(token), int(pos), kv, lg, _stream_handle(stream)))
+
+
+def amk_decode_step_noalloc(model: int, token: int, pos: int, kv_cache, logits_out, stream=None) -> None:
+    """As amk_decode_step, with the step's exchange words in the library's static device array."""
+    _check(lib().amk_decode_step_noalloc(model, int(token), int(pos), _ptr(kv_cache), _ptr(logits_out),
+                                         _stream_handle(stream)))
 
 
 def _ptr(x) -> int:

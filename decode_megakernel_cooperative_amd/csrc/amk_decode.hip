@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "amk_kparams.h"
@@ -1553,4 +1554,33 @@ extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(i
 
 extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle() {
   return (const void*)&amk::amk_clear_kernel;
+}
+
+// Exchange words and error flag of amk_decode_step_noalloc: one array per GPU, held until the
+// process ends, shared by every such call on that GPU. Host code never uses the array's name as
+// an address (in host code it is a stand-in, not device memory): amk_static_scratch looks the
+// device address up with hipGetSymbolAddress, once per device, and callers pass that pointer on.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Device address and size of `scratch` on the current device (looked up on the first call for a
+// device, then cached). Returns hipSuccess or the lookup's error.
+extern "C" __attribute__((visibility("hidden"))) hipError_t amk_static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
 }

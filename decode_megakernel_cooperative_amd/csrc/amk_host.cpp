@@ -17,6 +17,7 @@
 
 extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax);
 extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle();
+extern "C" __attribute__((visibility("hidden"))) hipError_t amk_static_scratch(void** ptr, size_t* bytes);
 
 namespace {
 
@@ -106,6 +107,8 @@ struct amk_model {
   uint8_t* scratch = nullptr;
   size_t scratch_bytes = 0;
   unsigned* herr = nullptr;  // pinned host word the first failing block of a launch writes its code to
+  uint8_t* static_scratch = nullptr;  // this device's static exchange array (amk_decode_step_noalloc)
+  size_t static_bytes = 0;
   float* dump = nullptr;     // per-stage dump (amk_set_dump), or null
   int64_t dump_layer = 0;    // floats per layer of the dump
   amk::KParams kp{};  // pointers and dims filled at load; step fields filled per call
@@ -372,6 +375,14 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   he = hipHostGetDevicePointer(reinterpret_cast<void**>(&herr_dev), m->herr, 0);
   if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_HIP, std::string("hipHostGetDevicePointer: ") + hipGetErrorString(he)); }
   m->dump_layer = 6 * H + QKV + 2 * QD + 3 * F;  // the slots of one layer in the dump
+  {  // set-up of the allocation-free step: this device's static exchange array (looked up once)
+    void* sp = nullptr;
+    size_t sb = 0;
+    he = amk_static_scratch(&sp, &sb);
+    if (he != hipSuccess) { amk_free(m); return fail(AMK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(he)); }
+    m->static_scratch = static_cast<uint8_t*>(sp);
+    m->static_bytes = sb;
+  }
 
   // ---------------- packing + upload ----------------
   std::vector<uint8_t> stage;
@@ -543,12 +554,17 @@ namespace {
 // Enqueues on `stream` the reset of the model's device state after a failed step: the error flag
 // and every exchange word go back to zero (after every launch already enqueued), and the tags
 // restart at 1, above the zero of a cleared word.
-int enqueue_reset(amk_model* m, void* stream) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(m->scratch);
-  size_t n = m->scratch_bytes / 4;
+int enqueue_clear(uint8_t* base, size_t bytes, void* stream) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(base);
+  size_t n = bytes / 4;
   void* args[] = {&p, &n};
   const unsigned blocks = static_cast<unsigned>(std::min<size_t>(1024, (n + 255) / 256));
   HIP_TRY(hipLaunchKernel(amk_clear_kernel_handle(), dim3(blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream)));
+  return AMK_OK;
+}
+int enqueue_reset(amk_model* m, void* stream) {
+  const int rc = enqueue_clear(m->scratch, m->scratch_bytes, stream);
+  if (rc) return rc;
   m->tag0 = 1;
   return AMK_OK;
 }
@@ -573,11 +589,28 @@ int take_pending_error(amk_model* m, void* stream) {
 
 // One decode step: a single cooperative launch. token_dev / next_token are null for a
 // host-token step. A pending failure of an earlier step is reported instead of launching.
+// With use_static, the launch keeps its exchange words and error flag in the device's static
+// array instead of the model's scratch: the used part is cleared first (a kernel, on the stream),
+// and the tags start at 1.
 int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t pos, void* kv_cache,
-                float* logits_out, int32_t* next_token, void* stream) {
+                float* logits_out, int32_t* next_token, void* stream, bool use_static = false) {
   const int pending = take_pending_error(m, stream);
   if (pending) return pending;
   amk::KParams k = m->kp;
+  if (use_static) {
+    const int rc = enqueue_clear(m->static_scratch, m->scratch_bytes, stream);
+    if (rc) return rc;
+    auto rebase = [&](auto* p) { return reinterpret_cast<decltype(p)>(m->static_scratch + (reinterpret_cast<uint8_t*>(p) - m->scratch)); };
+    k.err = rebase(k.err);
+    k.tagged = rebase(k.tagged);
+    k.tx = rebase(k.tx);
+    k.tq = rebase(k.tq);
+    k.tkv = rebase(k.tkv);
+    k.tpart = rebase(k.tpart);
+    k.to = rebase(k.to);
+    k.targ = rebase(k.targ);
+    k.tm = rebase(k.tm);
+  }
   k.token = token;
   k.token_dev = token_dev;
   k.next_token = next_token;
@@ -599,8 +632,12 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   k.trace_stride = m->trace_stride;
   k.dump = m->dump;
   k.dump_stride = m->dump_layer;
-  k.tag0 = m->tag0;
-  m->tag0 += static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
+  if (use_static) {
+    k.tag0 = 1;
+  } else {
+    k.tag0 = m->tag0;
+    m->tag0 += static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
+  }
   void* args[] = {&k};
   HIP_TRY(hipLaunchCooperativeKernel(m->kernel, dim3(m->grid), dim3(amk::kThreads), args,
                                      static_cast<unsigned>(m->lds_bytes), static_cast<hipStream_t>(stream)));
@@ -613,6 +650,19 @@ int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache, fl
   if (token < 0 || token >= m->cfg.vocab) return fail(AMK_ERR_INVALID_ARG, "token out of range");
   if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
   return launch_step(m, token, nullptr, pos, kv_cache, logits_out, nullptr, stream);
+}
+
+int amk_decode_step_noalloc(amk_model* m, int32_t token, int32_t pos, void* kv_cache, float* logits_out,
+                            void* stream) {
+  if (!m || !kv_cache || !logits_out) return fail(AMK_ERR_INVALID_ARG, "null handle or buffer");
+  if (token < 0 || token >= m->cfg.vocab) return fail(AMK_ERR_INVALID_ARG, "token out of range");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(AMK_ERR_INVALID_ARG, "pos out of range");
+  if (!m->static_scratch) return fail(AMK_ERR_HIP, "the static exchange array was not found at load");
+  if (m->scratch_bytes > m->static_bytes)
+    return fail(AMK_ERR_UNSUPPORTED, "the model needs " + std::to_string(m->scratch_bytes) +
+                                         " bytes of exchange words; the static array holds " +
+                                         std::to_string(m->static_bytes));
+  return launch_step(m, token, nullptr, pos, kv_cache, logits_out, nullptr, stream, true);
 }
 
 int amk_decode_step_greedy(amk_model* m, const int32_t* token_in, int32_t pos, void* kv_cache, float* logits_out,

@@ -165,6 +165,22 @@ int amk_validate_config(const amk_config* cfg, int32_t compute_units);
 int amk_decode_step(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
                     float* logits_out, void* stream);
 
+/* amk_decode_step for callers that cannot allocate device memory around a step: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. The same forward pass,
+ * arguments, outputs and host checks as amk_decode_step, but this call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine): the step's exchange words and error flag
+ * live in a file-scope static device array of the library (4 MiB per GPU, held until the process
+ * ends; its address is looked up once per device when a model is loaded) instead of the model's
+ * scratch. The call first clears the part the model uses (a kernel on `stream`), so it does not
+ * depend on what an earlier call on that GPU left there. Every such call on one GPU shares the
+ * array: calls that overlap in time on one GPU (other streams, other threads, other models) race
+ * and must not be issued. Errors: those of amk_decode_step, and UNSUPPORTED when the model needs
+ * more than 4 MiB of exchange words (no shape that amk_load_weights accepts on a 256-CU device
+ * needs more than 3 MiB). A failure of this call is reported like that of amk_decode_step (by
+ * the model's next call or amk_sync); it does not turn later calls into no-ops. */
+int amk_decode_step_noalloc(amk_model* m, int32_t token, int32_t pos, void* kv_cache,
+                            float* logits_out, void* stream);
+
 /* Greedy decode step with device-resident tokens (no host round trip per token): the same
  * forward pass as amk_decode_step, but the input token is read from device memory and the step
  * also writes the greedy next token: the argmax over the logits, with ties going to the lowest
