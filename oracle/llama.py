@@ -26,7 +26,9 @@ scale applied once after the fp32 sum; RoPE angles are computed in float64 and r
 fp32 cos/sin, with no frequency scaling; all seven per-layer projections and the lm_head are
 int8 under W8A16 while the embedding gather reads the bf16 table. W4A16 quantizes the seven
 projections to int4 codes with the same per-row rule (scale max|row| / 7) and keeps the lm_head
-bf16; its GEMV is the same s_n * sum_k q_nk x_k.
+bf16; its GEMV is the same s_n * sum_k q_nk x_k. W4A16-G128 quantizes them with one fp16 scale per
+group of 128 columns (oracle.quant) and keeps the lm_head bf16; its GEMV is the plain product
+with the dequantized weights, sum_k (q_nk * s_n,g(k)) x_k (each q * s is exact in fp32).
 """
 from __future__ import annotations
 
@@ -35,13 +37,14 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 from .numerics import bf16_bits_to_f32, f32_to_bf16_bits, round_bf16
-from .quant import quantize_rows_int4, quantize_rows_int8
+from .quant import dequantize_groups, quantize_rows_int4, quantize_rows_int4_g128, quantize_rows_int8
 
 F32 = np.float32
 FMT_BF16 = 0
 FMT_W8A16 = 1
 FMT_W8A16_BF16_HEAD = 2  # W8A16 projections, lm_head kept in bf16
 FMT_W4A16 = 3            # int4 projections (per-row scale), lm_head kept in bf16
+FMT_W4A16_G128 = 4       # int4 projections (fp16 scale per group of 128 columns), lm_head kept in bf16
 
 
 # ------------------------------------------------------------------------------------------
@@ -142,7 +145,10 @@ class Linear:
         self.fmt = fmt
         self.codes = self.scales = self.bits = None
         self._f32 = self._f64 = None
-        if fmt in (FMT_W8A16, FMT_W4A16):
+        if fmt == FMT_W4A16_G128:
+            self.codes, self.gscales = quantize_rows_int4_g128(bits)
+            self._f32 = dequantize_groups(self.codes, self.gscales)  # exact values, kept (rows x cols fp32)
+        elif fmt in (FMT_W8A16, FMT_W4A16):
             quantize = quantize_rows_int8 if fmt == FMT_W8A16 else quantize_rows_int4
             self.codes, self.scales = quantize(bits)
             if widen_once:
@@ -173,7 +179,7 @@ class Linear:
             r1 = min(self.rows, r0 + self.BLOCK)
             W = self._block(r0, r1, accum).astype(accum, copy=False)
             acc = xa @ W.T
-            if self.codes is not None:
+            if self.codes is not None and self.fmt != FMT_W4A16_G128:  # per-row scale after the sum
                 acc = acc * self.scales[r0:r1].astype(accum)
             y[..., r0:r1] = acc
         return y
@@ -203,7 +209,7 @@ class OracleModel:
         # (quantization / widening) over a thread pool, the arithmetic is the same
         mats = [tensors[1 + 9 * l + o] for l in range(L) for o in (1, 2, 3, 4, 6, 7, 8)] + [lm_bits]
         proj_fmt = {FMT_BF16: FMT_BF16, FMT_W8A16: FMT_W8A16, FMT_W8A16_BF16_HEAD: FMT_W8A16,
-                    FMT_W4A16: FMT_W4A16}[weight_format]
+                    FMT_W4A16: FMT_W4A16, FMT_W4A16_G128: FMT_W4A16_G128}[weight_format]
         lm_fmt = FMT_W8A16 if weight_format == FMT_W8A16 else FMT_BF16
         fmts = [proj_fmt] * (len(mats) - 1) + [lm_fmt]
         if threads > 1:

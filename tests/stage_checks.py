@@ -29,6 +29,7 @@ import numpy as np
 
 from oracle.llama import apply_rope, attention_head, rmsnorm, rope_tables, silu
 from oracle.numerics import bf16_bits_to_f32, round_bf16
+from oracle.quant import dequantize_groups
 
 SLOTS = ("h", "qkv", "q", "o", "wo", "xo", "h2", "gu", "m", "wd", "xd")
 
@@ -58,6 +59,8 @@ def sample_rows(n: int, seed: int, cap: int = 1024) -> np.ndarray:
 
 
 def _rows_f64(lin, rows):
+    if getattr(lin, "gscales", None) is not None:  # group-wise int4: the exact products q * s
+        return dequantize_groups(lin.codes[rows], lin.gscales[rows]).astype(np.float64), None
     if lin.codes is not None:
         return lin.codes[rows].astype(np.float64), lin.scales[rows].astype(np.float64)
     return bf16_bits_to_f32(lin.bits[rows]).astype(np.float64), None

@@ -18,6 +18,7 @@ import torch
 import oracle
 from oracle import llama as L
 from oracle.numerics import bf16_bits_to_f32, f32_to_bf16_bits, round_bf16
+from oracle.quant import (dequantize_groups, quantize_rows_int4_g128, quantize_rows_int4_g128_f32)
 from oracle.quant import (dequantize_rows, quantize_rows_int4, quantize_rows_int4_f32, quantize_rows_int8,
                           quantize_rows_int8_f32)
 import workloads as W
@@ -60,6 +61,21 @@ def test_bf16_round_matches_torch():
 # ------------------------------------------------------------------------------------------
 # C1 GEMV: brute force in float64 double loops on tiny non-square shapes
 # ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols", [(5, 300), (3, 128)])
+def test_gemv_brute_force_groups(rows, cols):
+    """Group-wise int4: y_n = sum_k q_nk s_n,g(k) x_k, by float64 double loops over the codes and
+    the fp16 group scales (groups of 128 columns; 300 columns end with a 44-column group)."""
+    wb = rng_bf16((rows, cols), 0.5, rows * cols + 9)
+    x = round_bf16(np.random.default_rng(2).standard_normal(cols).astype(np.float32))
+    lin = L.Linear(wb, L.FMT_W4A16_G128, widen_once=False)
+    y = lin.apply(x)
+    assert lin.gscales.shape == (rows, (cols + 127) // 128)
+    for r in range(rows):
+        terms = [float(lin.codes[r, c]) * float(lin.gscales[r, c // 128]) * float(x[c]) for c in range(cols)]
+        exact, absum = sum(terms), sum(abs(t) for t in terms)
+        assert abs(float(y[r]) - exact) <= cols * 2.0 ** -24 * absum + 1e-30, r
+
+
 @pytest.mark.parametrize("rows,cols", [(7, 13), (5, 64), (16, 33)])
 @pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16, L.FMT_W4A16])
 def test_gemv_brute_force(rows, cols, fmt):
@@ -244,6 +260,47 @@ def test_int4_quantizer_invariants_and_round_trip():
         assert np.allclose(s8 * np.float32(127 / 7), s, rtol=3e-7)
 
 
+def test_int4_g128_quantizer_worked_rows():
+    d = json.load(open(os.path.join(GOLDEN, "quant4g_tie_rows.json")))
+    for row in d["rows"]:
+        w = np.zeros(d["cols"], np.float32)
+        for k, v in row["nonzero_float"].items():
+            w[int(k)] = v
+        wb = to_bits(w[None])
+        assert np.array_equal(bf16_bits_to_f32(wb)[0], w)  # exact in bf16
+        codes, scales = quantize_rows_int4_g128(wb)
+        want = np.zeros(d["cols"], np.int8)
+        for k, v in row["codes_nonzero"].items():
+            want[int(k)] = v
+        assert np.array_equal(codes[0], want), row["why"]
+        assert np.array_equal(scales[0], np.array(row["scales"], np.float32)), row["why"]
+
+
+def test_int4_g128_invariants_and_round_trip():
+    for cols in (576, 2048, 4160):
+        wb = rng_bf16((96, cols), 0.02, cols + 3)
+        codes, s = quantize_rows_int4_g128(wb)
+        w = bf16_bits_to_f32(wb)
+        ng = (cols + 127) // 128
+        assert s.shape == (96, ng)
+        assert np.array_equal(s.astype(np.float16).astype(np.float32), s)  # fp16 values
+        assert codes.min() >= -7 and codes.max() <= 7
+        for g in range(ng):  # every nonzero group uses the full code range
+            assert np.all(np.max(np.abs(codes[:, g * 128:(g + 1) * 128].astype(np.int32)), axis=1) == 7)
+        sf = np.repeat(s, 128, axis=1)[:, :cols]
+        assert np.all(np.abs(w - dequantize_groups(codes, s)) <= sf * (0.5 + 1e-5))
+        c2, s2 = quantize_rows_int4_g128_f32(dequantize_groups(codes, s))
+        assert np.array_equal(c2, codes) and np.array_equal(s2, s)
+        # group scales track the local magnitude: a row whose first group is 64x larger keeps its
+        # other groups' codes, while a per-row scale flattens them
+        big = w.copy()
+        big[:, :128] *= 64
+        cb, sb = quantize_rows_int4_g128(to_bits(big))
+        assert np.array_equal(cb[:, 128:], codes[:, 128:])
+        cr, _ = quantize_rows_int4(to_bits(big))
+        assert np.mean(cr[:, 128:] == 0) > 0.9
+
+
 # ------------------------------------------------------------------------------------------
 # small-model helpers
 # ------------------------------------------------------------------------------------------
@@ -357,6 +414,40 @@ def test_int4_exact_codes_match_bf16_model():
     assert np.max(np.abs(a.decode_step(3, 0, kva) - b.decode_step(3, 0, kvb))) > 1e-2
 
 
+def test_int4_g128_exact_codes_match_bf16_model():
+    """Projections whose every group of 128 columns is k * 2^-m (|k| <= 7, one |k| = 7 in the
+    group, m varying by group) are exact group-wise int4 codes with s = 2^-m per group, so the
+    W4A16-G128 model equals the bf16 model on the same tensors to rounding; a per-row int4 scale
+    cannot represent them."""
+    shape = W.small_shape(hidden=256, n_layers=2, n_q_heads=2, n_kv_heads=1, head_dim=64, ffn=384, vocab=96,
+                          tied=False)
+    g = np.random.default_rng(19)
+    tensors = []
+    for i, (name, dims, kind) in enumerate(W.tensor_specs(shape)):
+        if kind == "norm":
+            tensors.append(to_bits(np.ones(dims, np.float32)))
+        elif i == len(W.tensor_specs(shape)) - 1 or i == 0:
+            tensors.append(rng_bf16(dims, 0.05, 190 + i))
+        else:
+            k = g.integers(-7, 8, dims).astype(np.float32)
+            e = np.repeat(-(7 + g.integers(0, 5, (dims[0], (dims[1] + 127) // 128))), 128, axis=1)[:, :dims[1]]
+            k[:, ::128] = np.where(g.random(k[:, ::128].shape) < 0.5, 7, -7)
+            tensors.append(to_bits(k * np.exp2(e).astype(np.float32)))
+    a = L.OracleModel(shape, tensors, L.FMT_BF16)
+    b = L.OracleModel(shape, tensors, L.FMT_W4A16_G128)
+    c = L.OracleModel(shape, tensors, L.FMT_W4A16)
+    lin = b.layers[1]["gate"]
+    assert lin.fmt == L.FMT_W4A16_G128 and b.lm_head.fmt == L.FMT_BF16
+    assert np.array_equal(dequantize_groups(lin.codes, lin.gscales), bf16_bits_to_f32(tensors[1 + 9 + 6]))
+    kva, kvb, kvc = fresh_kv(shape, 4), fresh_kv(shape, 4), fresh_kv(shape, 4)
+    worst_rowwise = 0.0
+    for pos, tok in enumerate([1, 50, 95]):
+        la, lb, lc = a.decode_step(tok, pos, kva), b.decode_step(tok, pos, kvb), c.decode_step(tok, pos, kvc)
+        assert np.allclose(la, lb, rtol=1e-5, atol=1e-5)
+        worst_rowwise = max(worst_rowwise, float(np.max(np.abs(la - lc))))
+    assert worst_rowwise > 1e-3
+
+
 def test_bf16_head_format_differs_only_in_the_head():
     """W8A16 with a bf16 lm_head: random (not exactly quantizable) projections, an lm_head of
     k * 2^-9 rows that int8 represents exactly. Only the head differs between the two formats and
@@ -421,7 +512,7 @@ def test_rope_scaling_factor_one_is_plain_rope():
 # ------------------------------------------------------------------------------------------
 # C8 decode step-by-step == independently written full-sequence causal forward
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16, L.FMT_W4A16])
+@pytest.mark.parametrize("fmt", [L.FMT_BF16, L.FMT_W8A16, L.FMT_W4A16, L.FMT_W4A16_G128])
 def test_decode_equals_prefill(fmt):
     shape = W.small_shape(hidden=64, n_layers=3, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=96, vocab=200)
     t = random_model_tensors(shape, seed=21, std=0.1)

@@ -30,7 +30,7 @@ def _dump(tr):
     return np.concatenate([np.asarray(p, np.float32).reshape(-1) for p in parts])
 
 
-@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_W8A16, W.FMT_W4A16])
+@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_W8A16, W.FMT_W4A16, W.FMT_W4A16_G128])
 def test_oracle_dump_passes(fmt):
     orc, tok, pos, tr, kv, logits = _traced_step(fmt)
     r = check_step(orc, SHAPE, tok, pos, _dump(tr), kv, logits, log=lambda *a: None)

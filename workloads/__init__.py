@@ -38,6 +38,7 @@ FMT_BF16 = 0
 FMT_W8A16 = 1
 FMT_W8A16_BF16_HEAD = 2  # W8A16 projections, bf16 lm_head
 FMT_W4A16 = 3            # int4 per-row projections, bf16 lm_head
+FMT_W4A16_G128 = 4       # int4 projections with an fp16 scale per group of 128 columns, bf16 lm_head
 
 
 @dataclass(frozen=True)
@@ -100,7 +101,7 @@ class Workload:
     @property
     def fmt_name(self) -> str:
         return {FMT_BF16: "bf16", FMT_W8A16: "w8a16", FMT_W8A16_BF16_HEAD: "w8a16-bf16head",
-                FMT_W4A16: "w4a16"}[self.weight_format]
+                FMT_W4A16: "w4a16", FMT_W4A16_G128: "w4a16-g128"}[self.weight_format]
 
 
 WORKLOADS = {
@@ -115,6 +116,9 @@ WORKLOADS = {
     # the pages' int4 weight-only variant (lossy, 2.42x less weight traffic than bf16)
     "smollm2-135m-w4a16": Workload("smollm2-135m-w4a16", SMOLLM2_135M, FMT_W4A16, 64, 0, 128),
     "llama3-8b-w4a16-ctx4096": Workload("llama3-8b-w4a16-ctx4096", LLAMA3_8B, FMT_W4A16, 0, 4096, 128),
+    # the same variant with group-wise scales (one fp16 scale per 128 columns of a row)
+    "smollm2-135m-w4a16g": Workload("smollm2-135m-w4a16g", SMOLLM2_135M, FMT_W4A16_G128, 64, 0, 128),
+    "llama3-8b-w4a16g-ctx4096": Workload("llama3-8b-w4a16g-ctx4096", LLAMA3_8B, FMT_W4A16_G128, 0, 4096, 128),
 }
 
 
