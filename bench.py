@@ -41,18 +41,22 @@ def log(*a):
 
 
 def algorithmic_bytes(shape, fmt: int, pos: int) -> int:
-    """Bytes one decode step at `pos` must move: every GEMV weight at storage width, the row
-    scales of quantized matrices, norm vectors, the embedding row, the K/V read over positions
-    [0, pos], the K/V write of position pos, and the fp32 logits. Activation scratch (KB per
-    stage) is excluded."""
+    """Bytes one decode step at `pos` must move: every GEMV weight at storage width, the scales of
+    quantized matrices (fp32 per row, or fp16 per row and 128 columns), norm vectors, the
+    embedding row, the K/V read over positions [0, pos], the K/V write of position pos, and the
+    fp32 logits. Activation scratch (KB per stage) is excluded."""
     H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
     qkv_rows = shape.q_dim + 2 * shape.kv_dim
-    wbits = {W.FMT_BF16: 16, W.FMT_W8A16: 8, W.FMT_W8A16_BF16_HEAD: 8, W.FMT_W4A16: 4}[fmt]  # projections
+    wbits = {W.FMT_BF16: 16, W.FMT_W8A16: 8, W.FMT_W8A16_BF16_HEAD: 8, W.FMT_W4A16: 4,
+             W.FMT_W4A16_G128: 4}[fmt]  # projections
     lmb = 1 if fmt == W.FMT_W8A16 else 2              # lm_head
     rows = L * (qkv_rows + H + 2 * F + H)
     mat = L * (qkv_rows * H + H * shape.q_dim + 2 * F * H + H * F)
     b = mat * wbits // 8 + V * H * lmb
-    if fmt != W.FMT_BF16:
+    if fmt == W.FMT_W4A16_G128:
+        groups = lambda k: (k + 127) // 128  # noqa: E731
+        b += 2 * L * (qkv_rows * groups(H) + H * groups(shape.q_dim) + 2 * F * groups(H) + H * groups(F))
+    elif fmt != W.FMT_BF16:
         b += 4 * rows
     if fmt == W.FMT_W8A16:
         b += 4 * V
@@ -272,7 +276,9 @@ def main() -> int:
         "config": {"workload": wl.key, "positions": f"{pos0}-{pos0 + steps - 1}", "batch": 1,
                    "weights": {W.FMT_BF16: "bf16", W.FMT_W8A16: "int8 per-row scales",
                                W.FMT_W8A16_BF16_HEAD: "int8 per-row scales, bf16 lm_head",
-                               W.FMT_W4A16: "int4 per-row scales, bf16 lm_head"}[fmt], "kv_cache": "bf16",
+                               W.FMT_W4A16: "int4 per-row scales, bf16 lm_head",
+                               W.FMT_W4A16_G128: "int4, fp16 scale per 128 columns, bf16 lm_head"}[fmt],
+                   "kv_cache": "bf16",
                    "grid": f"{info.grid_blocks}x{info.block_threads}",
                    "tokens": "device-resident greedy chain" if args.greedy else "host-fed, seeded"},
         "tokens_per_s": round(1e6 / us_per_token, 1),

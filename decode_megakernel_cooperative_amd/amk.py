@@ -27,10 +27,13 @@ AMK_BF16 = 0
 AMK_W8A16 = 1
 AMK_W8A16_BF16_HEAD = 2
 AMK_W4A16 = 3
+AMK_W4A16_G128 = 4
+GROUP = 128  # columns per group scale of AMK_W4A16_G128
 
 EXPORTED = ("amk_validate_config", "amk_load_weights", "amk_decode_step", "amk_decode_step_noalloc",
             "amk_decode_step_greedy", "amk_sync",
             "amk_kv_cache_bytes", "amk_get_info", "amk_export_quantized", "amk_quantize_int8", "amk_quantize_int4",
+            "amk_quantize_int4_g128",
             "amk_set_spin_limit", "amk_set_trace", "amk_set_dump", "amk_free", "amk_status_string")
 
 
@@ -81,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.amk_export_quantized.argtypes = [vp, i32, vp, vp]
         L.amk_quantize_int8.argtypes = [vp, i64, i64, vp, vp]
         L.amk_quantize_int4.argtypes = [vp, i64, i64, vp, vp]
+        L.amk_quantize_int4_g128.argtypes = [vp, i64, i64, vp, vp]
         L.amk_set_spin_limit.argtypes = [vp, ctypes.c_uint64]
         L.amk_set_trace.argtypes = [vp, vp, i32]
         L.amk_set_dump.argtypes = [vp, vp, i64]
@@ -175,9 +179,11 @@ def amk_get_info(model: int) -> amk_info:
     return info
 
 
-def amk_export_quantized(model: int, tensor_index: int, rows: int, cols: int):
+def amk_export_quantized(model: int, tensor_index: int, rows: int, cols: int, grouped: bool = False):
+    """codes int8 [rows, cols] and scales: fp32 [rows], or [rows, ceil(cols / 128)] when grouped
+    (a projection of an AMK_W4A16_G128 model)."""
     codes = np.empty((rows, cols), dtype=np.int8)
-    scales = np.empty(rows, dtype=np.float32)
+    scales = np.empty((rows, (cols + GROUP - 1) // GROUP) if grouped else rows, dtype=np.float32)
     _check(lib().amk_export_quantized(model, tensor_index, codes.ctypes.data, scales.ctypes.data))
     return codes, scales
 
@@ -197,6 +203,15 @@ def amk_quantize_int4(w_bits: np.ndarray):
     codes = np.empty((rows, cols), dtype=np.int8)
     scales = np.empty(rows, dtype=np.float32)
     _check(lib().amk_quantize_int4(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
+
+
+def amk_quantize_int4_g128(w_bits: np.ndarray):
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scales = np.empty((rows, (cols + GROUP - 1) // GROUP), dtype=np.float32)
+    _check(lib().amk_quantize_int4_g128(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data))
     return codes, scales
 
 

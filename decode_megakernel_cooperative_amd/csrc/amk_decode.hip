@@ -222,6 +222,12 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<0> { static constexpr int BITS = 16, CW = 512, LC = 8, NR = 1, XCS = 256; };    // bf16
 template <> struct Fmt<1> { static constexpr int BITS = 8, CW = 1024, LC = 16, NR = 4, XCS = 1024; };  // int8
 template <> struct Fmt<2> { static constexpr int BITS = 4, CW = 2048, LC = 32, NR = 4, XCS = 1024; };  // int4
+template <> struct Fmt<3> { static constexpr int BITS = 4, CW = 2048, LC = 32, NR = 4, XCS = 1024; };  // int4, group scales
+// Format 3 stores its codes as format 2 does; each run of 128 columns (four lanes' columns of a
+// chunk) has an fp16 scale per row. The 16 group scales of a chunk, for both rows of a pair, are
+// 64 bytes: dword j holds the scale of group j of row 0 (low half) and of row 1 (high half), and
+// the dwords of pair pr, chunk ch start at byte (pr * nch + ch) * 64 of the matrix's scale array.
+template <int FMT> constexpr bool kInt4 = FMT == 2 || FMT == 3;
 // int8 weights: the activations are fp32 in LDS. Column e is stored at chunk*CW + (k/4)*256 +
 // L*4 + k%4, k = e's index inside the lane, so the lane's k/4-th float4 sits at a 16-byte lane
 // stride: conflict-free ds_read_b128.
@@ -248,7 +254,7 @@ __device__ __forceinline__ int padded(int K) {
 // stores columns e .. e + 3 (e a multiple of 4).
 template <int FMT>
 __device__ __forceinline__ void put_x(float* xs, int e, float v) {
-  if constexpr (FMT == 2) reinterpret_cast<uint16_t*>(xs)[swz16(e)] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+  if constexpr (kInt4<FMT>) reinterpret_cast<uint16_t*>(xs)[swz16(e)] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
   else if constexpr (FMT == 0) reinterpret_cast<uint16_t*>(xs)[e] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
   else xs[swz<FMT>(e)] = v;
 }
@@ -257,7 +263,7 @@ __device__ __forceinline__ void put_x4(float* xs, int e, f32x4 v) {
   if constexpr (FMT != 1) {
     const uint32_t lo = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
     const uint32_t hi = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(xs) + (FMT == 2 ? swz16(e) : e)) = uint2{lo, hi};
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(xs) + (kInt4<FMT> ? swz16(e) : e)) = uint2{lo, hi};
   } else {
     *reinterpret_cast<f32x4*>(xs + swz<FMT>(e)) = v;
   }
@@ -554,6 +560,7 @@ constexpr int kSeg = 32; // pairs per operand window (lane j holds the operand o
 // the stage's input vector.
 struct GemvRegs {
   i32x4 a0[kCG], a1[kCG], b0[kCG], b1[kCG];
+  uint32_t sa[kCG], sb[kCG];  // group scales of the items' slots (format 3 only)
   float wA, wB;
 };
 
@@ -638,9 +645,22 @@ __device__ __forceinline__ void load_x(const float* __restrict__ xl, XSlot<FMT>&
 }
 
 template <int FMT>
-__device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const XSlot<FMT>& xs, float& a0,
-                                          float& a1) {
-  if constexpr (FMT == 2) {
+__device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const XSlot<FMT>& xs, uint32_t gs,
+                                          float& a0, float& a1) {
+  if constexpr (FMT == 3) {
+    // the lane's 32 columns lie in one group: their sum (in units of 2^-9), times the group's scale
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const i32x4 x = __builtin_bit_cast(i32x4, xs.v[d]);
+      p0 = dot8_i4(static_cast<uint32_t>(w0[d]), x, p0);
+      p1 = dot8_i4(static_cast<uint32_t>(w1[d]), x, p1);
+    }
+    const float s0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gs & 0xffffu)));
+    const float s1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gs >> 16)));
+    a0 = __builtin_fmaf(p0, s0, a0);
+    a1 = __builtin_fmaf(p1, s1, a1);
+  } else if constexpr (FMT == 2) {
     // dword d holds the lane's columns 8d .. 8d + 7; read d of the slot holds their activations
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -675,7 +695,7 @@ __device__ __forceinline__ void chunk_fma(const i32x4 w0, const i32x4 w1, const 
 }
 
 // Per-pair operands for a window of 32 pairs: lane j holds the value for row j & 1 of the
-// window's pair j / 2: A = the row scale of int8 / int4 weights, B = residual input (EPI_RESID) or RoPE cos
+// window's pair j / 2: A = the row scale of per-row int8 / int4 weights, B = residual input (EPI_RESID) or RoPE cos
 // (even j) / sin (odd j) of the pair (EPI_QKV).
 template <int FMT, int EPI>
 __device__ __forceinline__ void load_window(const KParams& p, const float* __restrict__ Sc, const GemvPlan& g,
@@ -686,7 +706,7 @@ __device__ __forceinline__ void load_window(const KParams& p, const float* __res
   A = 1.f;
   B = 0.f;
   if (k < g.pb) {
-    if (FMT != 0) A = Sc[row];  // int4: the epilogue applies the factor 2^9
+    if (FMT == 1 || FMT == 2) A = Sc[row];  // int4: the epilogue applies the factor 2^9
     if (EPI == EPI_RESID) {
       B = resid_from_embed ? bf16_to_f32(p.embed[static_cast<size_t>(step_token(p)) * p.H + row])
                            : ld_payload(p.tx + row);
@@ -777,10 +797,13 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
   }
 }
 
-// Issues the 8 loads of the item that starts at cursor c (advancing c by kCG slots). np = pairs
+// Issues the 8 loads of the item that starts at cursor c (advancing c by kCG slots), and for
+// format 3 the slots' group-scale dwords (lane L takes group L / 4 of the chunk). np = pairs
 // in the segment, base = first pair of the segment.
-__device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const GemvPlan& g, int base, int np,
-                                           Cursor& c, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG]) {
+template <int FMT>
+__device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t gsr, const GemvPlan& g,
+                                           int base, int np, Cursor& c, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG],
+                                           uint32_t (&gs)[kCG]) {
   const int lane = __lane_id();
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
@@ -788,9 +811,15 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const Gemv
     const int off = c.ch * 1024 + lane * 16;
     const int voff = (v && off < g.RB) ? off : kOOB;
     // uniform by construction; readfirstlane keeps the compiler from moving it to VGPRs
-    const int soff = __builtin_amdgcn_readfirstlane(v ? 2 * pidx(g, base + c.k) * g.RB : 0);
+    const int pr = v ? pidx(g, base + c.k) : 0;
+    const int soff = __builtin_amdgcn_readfirstlane(2 * pr * g.RB);
     r0[s] = ldbuf(rs, voff, soff);
     r1[s] = ldbuf(rs, voff, soff + g.RB);
+    if constexpr (FMT == 3) {
+      const int goff = __builtin_amdgcn_readfirstlane((pr * g.nch + c.ch) * 64);
+      gs[s] = static_cast<uint32_t>(
+          __builtin_amdgcn_raw_buffer_load_b32(gsr, v ? (lane >> 2) * 4 : kOOB, goff, kBufCacheNT));
+    }
     c.advance(g.cpp);
   }
 }
@@ -804,7 +833,7 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, const Gemv
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
                                              const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
-                                             float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
+                                             const uint32_t (&gs)[kCG], float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
                                              EpiState& st, XSlot<FMT>& xn, float* dp) {
   constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
@@ -820,17 +849,17 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
     }
     // keep the scheduler from hoisting the conversions of all slots at once (register spills)
     __builtin_amdgcn_sched_barrier(0);
-    chunk_fma<FMT>(r0[s], r1[s], xc, acc0, acc1);
+    chunk_fma<FMT>(r0[s], r1[s], xc, gs[s], acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
     if (c.ch == g.nch - 1 && c.k < np) {
       float y0 = wave_sum(acc0), y1 = wave_sum(acc1);
       acc0 = acc1 = 0.f;
       const int j = 2 * c.k;
-      if (FMT != 0) {
+      if (FMT == 1 || FMT == 2) {
         y0 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j));
         y1 *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wA), j + 1));
       }
-      if (FMT == 2) {  // the int4 products arrived as q * 2^-9 (exact)
+      if (kInt4<FMT>) {  // the int4 products arrived as q * 2^-9 (exact)
         y0 *= 512.f;
         y1 *= 512.f;
       }
@@ -845,12 +874,20 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
 // Loads the operand window of the segment at `base` and issues the segment's first two items.
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_segment_start(const KParams& p, __amdgpu_buffer_rsrc_t rs,
-                                                   const float* __restrict__ Sc, const GemvPlan& g, int base,
-                                                   int np, bool rfe, bool two, GemvRegs& R) {
+                                                   __amdgpu_buffer_rsrc_t gsr, const float* __restrict__ Sc,
+                                                   const GemvPlan& g, int base, int np, bool rfe, bool two,
+                                                   GemvRegs& R) {
   load_window<FMT, EPI>(p, Sc, g, base, rfe, R.wA, R.wB);
   Cursor c{0, 0};
-  gemv_issue(rs, g, base, np, c, R.a0, R.a1);
-  if (two) gemv_issue(rs, g, base, np, c, R.b0, R.b1);
+  gemv_issue<FMT>(rs, gsr, g, base, np, c, R.a0, R.a1, R.sa);
+  if (two) gemv_issue<FMT>(rs, gsr, g, base, np, c, R.b0, R.b1, R.sb);
+}
+
+// Buffer resource over a format-3 matrix's group scales (npairs * nch * 64 bytes); for the
+// other formats an empty resource that no load uses.
+template <int FMT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gscale_rsrc(const float* Sc, const GemvPlan& g, int npairs) {
+  return make_rsrc(Sc, FMT == 3 ? static_cast<uint32_t>(npairs * g.nch * 64) : 0u);
 }
 
 // Issues the stage's operand window and first two items; called before the block polls the
@@ -861,7 +898,8 @@ __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* _
                                               GemvRegs& R) {
   const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
-  gemv_segment_start<FMT, EPI>(p, rs, Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe, true, R);
+  gemv_segment_start<FMT, EPI>(p, rs, gscale_rsrc<FMT>(Sc, g, npairs), Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe,
+                               true, R);
 }
 
 // Runs the stage. Items alternate between the two register buffers, each refilled two items
@@ -875,10 +913,11 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
   const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
   EpiState st{-__builtin_inff(), 0x7fffffff};
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
+  const __amdgpu_buffer_rsrc_t gsr = gscale_rsrc<FMT>(Sc, g, npairs);
   const float* xlane = xs + __lane_id() * 4;
   for (int base = g.pa; base < g.pb; base += kSeg) {
     const int np = min(kSeg, g.pb - base);
-    if (base != g.pa) gemv_segment_start<FMT, EPI>(p, rs, Sc, g, base, np, rfe, true, R);
+    if (base != g.pa) gemv_segment_start<FMT, EPI>(p, rs, gsr, Sc, g, base, np, rfe, true, R);
     const int items = (np * g.cpp + kCG - 1) / kCG;
     Cursor ci{0, 0}, cc{0, 0};
     for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
@@ -887,10 +926,12 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
     XSlot<FMT> xn;
     load_x<FMT>(xlane, xn);  // slot 0 of the segment is chunk 0
     for (int it = 0; it < items; it += 2) {
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn, dp);
-      gemv_issue(rs, g, base, np, ci, R.a0, R.a1);
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.wA, R.wB, cc, acc0, acc1, tg, st, xn, dp);
-      gemv_issue(rs, g, base, np, ci, R.b0, R.b1);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.sa, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
+                             dp);
+      gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
+      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
+                             dp);
+      gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
     }
   }
   return st;
@@ -1524,6 +1565,10 @@ template __global__ void amk_decode_kernel<64, 2, 4>(const KParams);
 template __global__ void amk_decode_kernel<128, 2, 4>(const KParams);
 template __global__ void amk_decode_kernel<64, 2, 8>(const KParams);
 template __global__ void amk_decode_kernel<128, 2, 8>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 4>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 4>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 8>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 8>(const KParams);
 
 // Zeroes n 32-bit words (a model's scratch: error flag and exchange words) before the model is
 // used again after a failure; a kernel rather than a memset so that it is safe in graph capture.
@@ -1536,19 +1581,19 @@ __global__ void amk_clear_kernel(uint32_t* p, size_t n) {
 }  // namespace amk
 
 // host-visible handles of the kernel instantiations (defined in this translation unit)
-// fmt: 0 bf16, 1 int8, 2 int4 projection weights
+// fmt: 0 bf16, 1 int8, 2 int4 (row scales), 3 int4 (group scales) projection weights
 extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax) {
   using namespace amk;
-  const void* const t[2][2][3] = {
+  const void* const t[2][2][4] = {
       {{(const void*)&amk_decode_kernel<64, 0, 4>, (const void*)&amk_decode_kernel<64, 1, 4>,
-        (const void*)&amk_decode_kernel<64, 2, 4>},
+        (const void*)&amk_decode_kernel<64, 2, 4>, (const void*)&amk_decode_kernel<64, 3, 4>},
        {(const void*)&amk_decode_kernel<64, 0, 8>, (const void*)&amk_decode_kernel<64, 1, 8>,
-        (const void*)&amk_decode_kernel<64, 2, 8>}},
+        (const void*)&amk_decode_kernel<64, 2, 8>, (const void*)&amk_decode_kernel<64, 3, 8>}},
       {{(const void*)&amk_decode_kernel<128, 0, 4>, (const void*)&amk_decode_kernel<128, 1, 4>,
-        (const void*)&amk_decode_kernel<128, 2, 4>},
+        (const void*)&amk_decode_kernel<128, 2, 4>, (const void*)&amk_decode_kernel<128, 3, 4>},
        {(const void*)&amk_decode_kernel<128, 0, 8>, (const void*)&amk_decode_kernel<128, 1, 8>,
-        (const void*)&amk_decode_kernel<128, 2, 8>}}};
-  if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 2) return nullptr;
+        (const void*)&amk_decode_kernel<128, 2, 8>, (const void*)&amk_decode_kernel<128, 3, 8>}}};
+  if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 3) return nullptr;
   return t[head_dim == 128][gmax == 8][fmt];
 }
 

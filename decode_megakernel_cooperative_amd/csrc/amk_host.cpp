@@ -71,6 +71,54 @@ void quantize_rows(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8
   }
 }
 
+// fp32 -> IEEE half, round to nearest even, for finite |f| <= 65504 (the group-scale range).
+uint16_t f32_to_f16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
+  if (a < 0x38800000u) {  // below 2^-14: a multiple of 2^-24 (the exact scaling rounds once)
+    const float m = std::nearbyint(std::fabs(f) * 16777216.0f);
+    return static_cast<uint16_t>(sign | static_cast<uint32_t>(m));  // 1024 encodes 2^-14 itself
+  }
+  const uint32_t r = a + 0xfffu + ((a >> 13) & 1u);  // round the 13 dropped bits to nearest even
+  return static_cast<uint16_t>(sign | ((r - (112u << 23)) >> 13));
+}
+float f16_to_f32(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  const float v = e == 0 ? std::ldexp(static_cast<float>(m), -24) : std::ldexp(static_cast<float>(1024 + m), e - 25);
+  return (h & 0x8000u) ? -v : v;
+}
+
+constexpr int64_t kGroup = 128;  // columns per int4 group scale
+
+// Group-wise int4 quantizer for rows [r0, r1): per 128-column group, s = fp16(amax / 7) (IEEE
+// fp32 division, then nearest-even half; saturating at 65504), q = clamp(nearbyint(w / s), -7,
+// 7); s == 0 gives q = 0. scales: fp32 [rows][ceil(cols / 128)] holding the half values.
+void quantize_groups(const uint16_t* w, int64_t cols, int64_t r0, int64_t r1, int8_t* codes, float* scales) {
+  const int64_t ng = (cols + kGroup - 1) / kGroup;
+  for (int64_t r = r0; r < r1; ++r) {
+    const uint16_t* row = w + r * cols;
+    int8_t* out = codes + r * cols;
+    for (int64_t g = 0; g < ng; ++g) {
+      const int64_t c0 = g * kGroup, c1 = std::min(cols, c0 + kGroup);
+      float amax = 0.f;
+      for (int64_t c = c0; c < c1; ++c) amax = std::max(amax, std::fabs(bf16_to_float(row[c])));
+      volatile float denom = 7.0f;  // a true division
+      const float s = f16_to_f32(f32_to_f16(std::min(amax / denom, 65504.0f)));
+      scales[r * ng + g] = s;
+      for (int64_t c = c0; c < c1; ++c) {
+        float q = 0.f;
+        if (s != 0.f) q = std::min(7.0f, std::max(-7.0f, std::nearbyint(bf16_to_float(row[c]) / s)));
+        out[c] = static_cast<int8_t>(q);
+      }
+    }
+  }
+}
+
+// Bytes of a format-3 (group-scaled int4) matrix's packed scales: 64 per row pair and 2048-column
+// chunk.
+inline int64_t gscale_bytes(int64_t rows, int64_t cols) { return rows / 2 * ((cols + 2047) / 2048) * 64; }
+
 template <typename F>
 void parallel_rows(int64_t rows, F&& f) {
   const unsigned hw = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
@@ -133,10 +181,11 @@ int validate_config(const amk_config* c) {
   if (c->ffn > 32768 || c->n_q_heads * c->head_dim > 32768) return fail(AMK_ERR_UNSUPPORTED, "ffn or q dim > 32768");
   if (c->vocab % 2) return fail(AMK_ERR_UNSUPPORTED, "vocab must be even");
   if (c->weight_format != AMK_BF16 && c->weight_format != AMK_W8A16 && c->weight_format != AMK_W8A16_BF16_HEAD &&
-      c->weight_format != AMK_W4A16)
+      c->weight_format != AMK_W4A16 && c->weight_format != AMK_W4A16_G128)
     return fail(AMK_ERR_UNSUPPORTED, "weight_format");
-  if (c->weight_format == AMK_W4A16 && (c->hidden % 32 || c->ffn % 32 || (c->n_q_heads * c->head_dim) % 32))
-    return fail(AMK_ERR_UNSUPPORTED, "W4A16 needs hidden, ffn and n_q_heads*head_dim multiples of 32");
+  const bool int4 = c->weight_format == AMK_W4A16 || c->weight_format == AMK_W4A16_G128;
+  if (int4 && (c->hidden % 32 || c->ffn % 32 || (c->n_q_heads * c->head_dim) % 32))
+    return fail(AMK_ERR_UNSUPPORTED, "int4 weights need hidden, ffn and n_q_heads*head_dim multiples of 32");
   if (c->rope_scale_factor > 1.0f &&
       !(c->rope_low_freq_factor > 0.0f && c->rope_high_freq_factor > c->rope_low_freq_factor &&
         c->rope_original_ctx > 0))
@@ -146,7 +195,7 @@ int validate_config(const amk_config* c) {
   // of the cache through buffer resources with 32-bit byte offsets
   const int64_t H = c->hidden, F = c->ffn, V = c->vocab, hd = c->head_dim;
   const int64_t QD = c->n_q_heads * hd, QKV = QD + 2 * c->n_kv_heads * hd;
-  const int64_t pbits = c->weight_format == AMK_BF16 ? 16 : (c->weight_format == AMK_W4A16 ? 4 : 8);
+  const int64_t pbits = c->weight_format == AMK_BF16 ? 16 : (int4 ? 4 : 8);
   const int64_t lm_bits = c->weight_format == AMK_W8A16 ? 8 : 16;
   const int64_t lim = int64_t(1) << 31;
   if (QKV * H * pbits / 8 >= lim || H * QD * pbits / 8 >= lim || 2 * F * H * pbits / 8 >= lim ||
@@ -260,6 +309,13 @@ int amk_quantize_int4(const uint16_t* w, int64_t rows, int64_t cols, int8_t* cod
   return AMK_OK;
 }
 
+int amk_quantize_int4_g128(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes, float* scales) {
+  if (!w || !codes || !scales) return fail(AMK_ERR_INVALID_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0) return fail(AMK_ERR_INVALID_ARG, "non-positive size");
+  parallel_rows(rows, [&](int64_t a, int64_t b) { quantize_groups(w, cols, a, b, codes, scales); });
+  return AMK_OK;
+}
+
 int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_tensors, amk_model** out) {
   if (!out) return fail(AMK_ERR_INVALID_ARG, "null out");
   *out = nullptr;
@@ -277,8 +333,9 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   const int64_t QKV = QD + 2 * KD;
   const bool q8 = c.weight_format != AMK_BF16;         // quantized projections (int8 or int4)
   const bool lm_q8 = c.weight_format == AMK_W8A16;     // int8 lm_head
-  const int pbits = c.weight_format == AMK_BF16 ? 16 : (c.weight_format == AMK_W4A16 ? 4 : 8);  // projections
-  const int kfmt = pbits == 16 ? 0 : (pbits == 8 ? 1 : 2);  // kernel weight format
+  const bool grp = c.weight_format == AMK_W4A16_G128;  // int4 with group scales
+  const int pbits = c.weight_format == AMK_BF16 ? 16 : (c.weight_format == AMK_W4A16 || grp ? 4 : 8);  // projections
+  const int kfmt = pbits == 16 ? 0 : (pbits == 8 ? 1 : (grp ? 3 : 2));  // kernel weight format
 
   auto m = new amk_model();
   m->cfg = c;
@@ -303,11 +360,16 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   m->off_d = take(l_d * L);
   const bool lm_shares_embed = !lm_q8 && c.tied_embeddings;
   m->off_lm = lm_shares_embed ? off_embed : take(static_cast<size_t>(V * H * (lm_q8 ? 1 : 2)));
+  // per-layer scale bytes: fp32 row scales, or the packed group scales of format 3
+  const size_t sl_qkv = static_cast<size_t>(grp ? gscale_bytes(QKV, H) : 4 * QKV);
+  const size_t sl_o = static_cast<size_t>(grp ? gscale_bytes(H, QD) : 4 * H);
+  const size_t sl_gu = static_cast<size_t>(grp ? gscale_bytes(2 * F, H) : 4 * 2 * F);
+  const size_t sl_d = static_cast<size_t>(grp ? gscale_bytes(H, F) : 4 * H);
   if (q8) {
-    m->off_sqkv = take(4 * QKV * L);
-    m->off_so = take(4 * H * L);
-    m->off_sgu = take(4 * 2 * F * L);
-    m->off_sd = take(4 * H * L);
+    m->off_sqkv = take(sl_qkv * L);
+    m->off_so = take(sl_o * L);
+    m->off_sgu = take(sl_gu * L);
+    m->off_sd = take(sl_d * L);
   }
   if (lm_q8) m->off_slm = take(4 * V);
   const size_t off_nin = take(4 * H * L), off_npost = take(4 * H * L), off_nfin = take(4 * H);
@@ -396,29 +458,40 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   };
   // Packs rows of one layer's matrix given a row map (packed row -> source pointer).
   // bits: 16 (bf16 rows copied), 8 (int8 codes) or 4 (int4 codes, eight per 32-bit word in the
-  // sign-magnitude layout of pack_int4_word)
-  auto pack_matrix = [&](int bits, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
+  // sign-magnitude layout of pack_int4_word); gs: group scales (format 3) instead of row scales
+  auto pack_matrix = [&](int bits, bool gs, int64_t rows, int64_t cols, size_t dst_w, size_t dst_s,
                          const std::vector<const uint16_t*>& src_tensors,
                          auto&& row_source) -> int {
     if (bits != 16) {
       // quantize each source tensor in canonical order, then permute rows
+      const int64_t ns = gs ? (cols + kGroup - 1) / kGroup : 1;  // scales per row
       std::vector<std::vector<int8_t>> qc(src_tensors.size());
       std::vector<std::vector<float>> qs(src_tensors.size());
       for (size_t k = 0; k < src_tensors.size(); ++k) {
         int64_t r_k = 0;
         for (int64_t r = 0; r < rows; ++r) { int w; int64_t sr; row_source(r, &w, &sr); if (w == static_cast<int>(k)) ++r_k; }
         qc[k].resize(static_cast<size_t>(r_k * cols));
-        qs[k].resize(static_cast<size_t>(r_k));
+        qs[k].resize(static_cast<size_t>(r_k * ns));
         int e = bits == 8 ? amk_quantize_int8(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data())
+                : gs      ? amk_quantize_int4_g128(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data())
                           : amk_quantize_int4(src_tensors[k], r_k, cols, qc[k].data(), qs[k].data());
         if (e) return e;
       }
       codes.resize(static_cast<size_t>(rows * cols));
-      scales.resize(static_cast<size_t>(rows));
+      scales.resize(static_cast<size_t>(rows * ns));
       for (int64_t r = 0; r < rows; ++r) {
         int w; int64_t sr; row_source(r, &w, &sr);
         std::memcpy(codes.data() + r * cols, qc[w].data() + sr * cols, static_cast<size_t>(cols));
-        scales[static_cast<size_t>(r)] = qs[w][static_cast<size_t>(sr)];
+        std::memcpy(scales.data() + r * ns, qs[w].data() + sr * ns, static_cast<size_t>(ns) * 4);
+      }
+      std::vector<uint16_t> gpk;
+      if (gs) {  // pair pr, chunk ch: 16 dwords (row 0 scale | row 1 scale << 16) of groups 16 ch ..
+        const int64_t nch = (cols + 2047) / 2048;
+        gpk.assign(static_cast<size_t>(gscale_bytes(rows, cols) / 2), 0);
+        for (int64_t r = 0; r < rows; ++r)
+          for (int64_t g = 0; g < ns; ++g)
+            gpk[static_cast<size_t>((((r / 2) * nch + g / 16) * 16 + g % 16) * 2 + (r & 1))] =
+                f32_to_f16(scales[static_cast<size_t>(r * ns + g)]);
       }
       if (bits == 4) {  // eight codes per word, in place (word i is written after codes 8i .. 8i + 7 are read)
         const int64_t n = rows * cols / 8;
@@ -429,6 +502,7 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
       }
       int e = upload(dst_w, codes.data(), static_cast<size_t>(rows * cols * bits / 8));
       if (e) return e;
+      if (gs) return upload(dst_s, gpk.data(), gpk.size() * 2);
       return upload(dst_s, scales.data(), static_cast<size_t>(rows) * 4);
     }
     stage.resize(static_cast<size_t>(rows * cols * 2));
@@ -447,23 +521,23 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
       nin[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[0][i]);
       npost[static_cast<size_t>(l * H + i)] = bf16_to_float(lt[5][i]);
     }
-    rc = pack_matrix(pbits, QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + 4 * QKV * l, {lt[1], lt[2], lt[3]},
+    rc = pack_matrix(pbits, grp, QKV, H, m->off_qkv + l * l_qkv, m->off_sqkv + sl_qkv * l, {lt[1], lt[2], lt[3]},
                      [&](int64_t r, int* w, int64_t* sr) { qkv_source(c, r, w, sr); });
     if (rc) break;
-    rc = pack_matrix(pbits, H, QD, m->off_o + l * l_o, m->off_so + 4 * H * l, {lt[4]},
+    rc = pack_matrix(pbits, grp, H, QD, m->off_o + l * l_o, m->off_so + sl_o * l, {lt[4]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
     if (rc) break;
-    rc = pack_matrix(pbits, 2 * F, H, m->off_gu + l * l_gu, m->off_sgu + 4 * 2 * F * l, {lt[6], lt[7]},
+    rc = pack_matrix(pbits, grp, 2 * F, H, m->off_gu + l * l_gu, m->off_sgu + sl_gu * l, {lt[6], lt[7]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = static_cast<int>(r & 1); *sr = r >> 1; });
     if (rc) break;
-    rc = pack_matrix(pbits, H, F, m->off_d + l * l_d, m->off_sd + 4 * H * l, {lt[8]},
+    rc = pack_matrix(pbits, grp, H, F, m->off_d + l * l_d, m->off_sd + sl_d * l, {lt[8]},
                      [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) {
     for (int64_t i = 0; i < H; ++i) nfin[static_cast<size_t>(i)] = bf16_to_float(t[1 + 9 * L][i]);
     const uint16_t* lm = c.tied_embeddings ? t[0] : t[2 + 9 * L];
     if (!lm_shares_embed)
-      rc = pack_matrix(lm_q8 ? 8 : 16, V, H, m->off_lm, m->off_slm, {lm},
+      rc = pack_matrix(lm_q8 ? 8 : 16, false, V, H, m->off_lm, m->off_slm, {lm},
                        [&](int64_t r, int* w, int64_t* sr) { *w = 0; *sr = r; });
   }
   if (rc == AMK_OK) rc = upload(off_nin, nin.data(), nin.size() * 4);
@@ -519,10 +593,11 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   k.w_d = W + m->off_d; k.w_d_ls = static_cast<int64_t>(l_d);
   k.w_lm = W + m->off_lm;
   if (q8) {
-    k.s_qkv = reinterpret_cast<const float*>(W + m->off_sqkv); k.s_qkv_ls = QKV;
-    k.s_o = reinterpret_cast<const float*>(W + m->off_so); k.s_o_ls = H;
-    k.s_gu = reinterpret_cast<const float*>(W + m->off_sgu); k.s_gu_ls = 2 * F;
-    k.s_d = reinterpret_cast<const float*>(W + m->off_sd); k.s_d_ls = H;
+    // layer strides in floats (the packed group scales are whole dwords too)
+    k.s_qkv = reinterpret_cast<const float*>(W + m->off_sqkv); k.s_qkv_ls = static_cast<int64_t>(sl_qkv / 4);
+    k.s_o = reinterpret_cast<const float*>(W + m->off_so); k.s_o_ls = static_cast<int64_t>(sl_o / 4);
+    k.s_gu = reinterpret_cast<const float*>(W + m->off_sgu); k.s_gu_ls = static_cast<int64_t>(sl_gu / 4);
+    k.s_d = reinterpret_cast<const float*>(W + m->off_sd); k.s_d_ls = static_cast<int64_t>(sl_d / 4);
   }
   if (lm_q8) k.s_lm = reinterpret_cast<const float*>(W + m->off_slm);
   k.lm_fmt = lm_q8 ? 1 : 0;
@@ -724,8 +799,11 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
   const int L = c.n_layers;
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hd = c.head_dim;
   const int64_t QD = c.n_q_heads * hd, KD = c.n_kv_heads * hd, QKV = QD + 2 * KD;
-  const int pbits = c.weight_format == AMK_W4A16 ? 4 : 8;  // projection code width
+  const bool grp = c.weight_format == AMK_W4A16_G128;
+  const int pbits = c.weight_format == AMK_W4A16 || grp ? 4 : 8;  // projection code width
   auto lb = [&](int64_t n) { return static_cast<size_t>(n * pbits / 8); };  // bytes of n codes
+  // bytes of one layer's scales of a matrix
+  auto sb = [&](int64_t r, int64_t k) { return static_cast<size_t>(grp ? gscale_bytes(r, k) : 4 * r); };
   const int lm_idx = c.tied_embeddings ? 0 : 2 + 9 * L;
   int64_t rows = 0, cols = 0, mrows = 0;
   size_t wsrc = 0, ssrc = 0;
@@ -739,21 +817,33 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
     switch (o) {
       case 1: case 2: case 3:
         kind = 0; which = o - 1; rows = (o == 1) ? QD : KD; cols = H; mrows = QKV;
-        wsrc = m->off_qkv + l * lb(QKV * H); ssrc = m->off_sqkv + 4 * static_cast<size_t>(QKV) * l; break;
-      case 4: kind = 1; rows = mrows = H; cols = QD; wsrc = m->off_o + l * lb(H * QD); ssrc = m->off_so + 4 * static_cast<size_t>(H) * l; break;
+        wsrc = m->off_qkv + l * lb(QKV * H); ssrc = m->off_sqkv + sb(QKV, H) * l; break;
+      case 4: kind = 1; rows = mrows = H; cols = QD; wsrc = m->off_o + l * lb(H * QD); ssrc = m->off_so + sb(H, QD) * l; break;
       case 6: case 7:
         kind = 2; which = o - 6; rows = F; cols = H; mrows = 2 * F;
-        wsrc = m->off_gu + l * lb(2 * F * H); ssrc = m->off_sgu + 4 * static_cast<size_t>(2 * F) * l; break;
-      case 8: kind = 3; rows = mrows = H; cols = F; wsrc = m->off_d + l * lb(H * F); ssrc = m->off_sd + 4 * static_cast<size_t>(H) * l; break;
+        wsrc = m->off_gu + l * lb(2 * F * H); ssrc = m->off_sgu + sb(2 * F, H) * l; break;
+      case 8: kind = 3; rows = mrows = H; cols = F; wsrc = m->off_d + l * lb(H * F); ssrc = m->off_sd + sb(H, F) * l; break;
       default: break;
     }
   }
   if (kind < 0) return fail(AMK_ERR_INVALID_ARG, "tensor index is not a quantized matrix");
   const int bits = kind == 4 ? 8 : pbits;
+  const bool gs = grp && kind != 4;
+  const int64_t ns = gs ? (cols + kGroup - 1) / kGroup : 1;  // scales per row
   std::vector<int8_t> allc(static_cast<size_t>(mrows * cols));
-  std::vector<float> alls(static_cast<size_t>(mrows));
+  std::vector<float> alls(static_cast<size_t>(mrows * ns));
   HIP_TRY(hipMemcpy(allc.data(), m->weights + wsrc, static_cast<size_t>(mrows * cols * bits / 8), hipMemcpyDeviceToHost));
-  HIP_TRY(hipMemcpy(alls.data(), m->weights + ssrc, alls.size() * 4, hipMemcpyDeviceToHost));
+  if (gs) {  // unpack the pair-chunk layout of the group scales
+    const int64_t nch = (cols + 2047) / 2048;
+    std::vector<uint16_t> gpk(static_cast<size_t>(gscale_bytes(mrows, cols) / 2));
+    HIP_TRY(hipMemcpy(gpk.data(), m->weights + ssrc, gpk.size() * 2, hipMemcpyDeviceToHost));
+    for (int64_t r = 0; r < mrows; ++r)
+      for (int64_t g = 0; g < ns; ++g)
+        alls[static_cast<size_t>(r * ns + g)] =
+            f16_to_f32(gpk[static_cast<size_t>((((r / 2) * nch + g / 16) * 16 + g % 16) * 2 + (r & 1))]);
+  } else {
+    HIP_TRY(hipMemcpy(alls.data(), m->weights + ssrc, alls.size() * 4, hipMemcpyDeviceToHost));
+  }
   if (bits == 4)  // unpack in place from the back: word i holds codes 8i .. 8i + 7
     for (int64_t i = mrows * cols / 8 - 1; i >= 0; --i) {
       uint32_t w;
@@ -767,7 +857,7 @@ int amk_export_quantized(const amk_model* m, int32_t idx, int8_t* codes_out, flo
     else if (kind == 2) { w = static_cast<int>(r & 1); sr = r >> 1; }
     if (which >= 0 && w != which) continue;
     std::memcpy(codes_out + sr * cols, allc.data() + r * cols, static_cast<size_t>(cols));
-    scales_out[sr] = alls[static_cast<size_t>(r)];
+    std::memcpy(scales_out + sr * ns, alls.data() + r * ns, static_cast<size_t>(ns) * 4);
   }
   (void)rows;
   return AMK_OK;

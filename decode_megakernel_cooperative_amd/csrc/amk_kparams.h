@@ -26,7 +26,8 @@ struct KParams {
   int32_t* next_token;                      // greedy step: argmax of the logits (else null)
   // packed weights: per layer, rows are stored in the order the kernel consumes them
   const uint8_t* w_qkv; int64_t w_qkv_ls;   // bytes per layer
-  const float* s_qkv;   int64_t s_qkv_ls;   // fp32 row scales per layer (int8 / int4 weights only)
+  const float* s_qkv;   int64_t s_qkv_ls;   // per layer: fp32 row scales, or the packed fp16 group
+                                            // scales of format 3 (stride in floats)
   const uint8_t* w_o;   int64_t w_o_ls;
   const float* s_o;     int64_t s_o_ls;
   const uint8_t* w_gu;  int64_t w_gu_ls;

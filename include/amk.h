@@ -46,6 +46,8 @@ extern "C" {
                                  head reads the bf16 embedding table; no quantized copy)      */
 #define AMK_W4A16 3 /* projections int4 (eight codes per word), one fp32 scale per output row;
                        lm_head kept bf16 as in AMK_W8A16_BF16_HEAD; activations bf16           */
+#define AMK_W4A16_G128 4 /* projections int4 as in AMK_W4A16, one fp16 scale per row and group
+                            of 128 columns; lm_head kept bf16; activations bf16               */
 
 /* Model description. Weights follow HuggingFace LlamaForCausalLM: pre-norm RMSNorm,
  * rotate-half RoPE with inv_freq_i = rope_theta^(-2i/head_dim), grouped-query attention
@@ -64,7 +66,8 @@ typedef struct {
   float rms_eps;           /* RMSNorm epsilon                                                */
   float rope_theta;        /* RoPE base                                                      */
   int32_t tied_embeddings; /* 1: lm_head is embed_tokens                                     */
-  int32_t weight_format;   /* AMK_BF16, AMK_W8A16, AMK_W8A16_BF16_HEAD or AMK_W4A16          */
+  int32_t weight_format;   /* AMK_BF16, AMK_W8A16, AMK_W8A16_BF16_HEAD, AMK_W4A16 or
+                              AMK_W4A16_G128                                                 */
   /* Llama-3 RoPE frequency scaling (the rule Llama 3.1 / 3.2 checkpoints declare; the pages do
    * not describe it): rope_scale_factor <= 1 means none. Otherwise a frequency f with
    * wavelength 2 pi / f shorter than rope_original_ctx / rope_high_freq_factor is kept, one
@@ -93,7 +96,7 @@ typedef struct {
   int64_t dump_floats;          /* floats of a whole dump: n_layers * dump_layer_floats + H  */
 } amk_info;
 
-/* Copies, packs, (for the W8A16 formats) quantizes and uploads a model to the current device.
+/* Copies, packs, (for the quantized formats) quantizes and uploads a model to the current device.
  * host_bf16_tensors: n_tensors host pointers to bf16 bit patterns (uint16), row-major
  *   [out][in] for matrices, in canonical HF order:
  *     embed_tokens [V][H];
@@ -114,11 +117,16 @@ typedef struct {
  * weight bytes of a SmolLM2-135M or Llama-3.2-1B shape). Device row layout: columns 8i .. 8i + 7
  * in 32-bit word i; byte k of a word holds |q| of column k in bits 0..2 and its sign in bit 7,
  * |q| of column k + 4 in bits 4..6, and the sign of column (k + 3) mod 4 + 4 in bit 3.
+ * AMK_W4A16_G128 quantizes the projections with amk_quantize_int4_g128 (one scale per 128
+ * columns) and keeps the lm_head bf16: the same codes and code layout as AMK_W4A16, plus 2
+ * bytes of scale per 128 weights, 1/2.415 of the bf16 weight bytes on those two shapes. The
+ * device holds the 16 scales of each 2048-column chunk of a row pair (both rows) together, 64
+ * bytes per pair and chunk.
  * Synchronous. The caller keeps ownership of its host tensors (they may be freed on return);
  * *out receives a model handle owned by the library until amk_free.
  * Errors: INVALID_ARG (null pointers, wrong n_tensors); UNSUPPORTED for a shape outside the
  * supported set: head_dim in {64,128}, nq % nkv == 0, nq/nkv <= 8, hidden, ffn and nq*hd
- * multiples of 16 (of 32 for AMK_W4A16), vocab even, hidden <= 8192, ffn and nq*hd <= 32768,
+ * multiples of 16 (of 32 for AMK_W4A16 and AMK_W4A16_G128), vocab even, hidden <= 8192, ffn and nq*hd <= 32768,
  * every packed weight matrix, the embedding and each (layer, K/V, kv head) block of the cache
  * below 2^31 bytes (the kernel addresses them with 32-bit offsets); and, on the current device
  * with G compute units (one persistent block each): nkv <= G, ffn >= G, and for n_layers >= 2
@@ -213,12 +221,13 @@ size_t amk_kv_cache_bytes(const amk_model* m);
 /* Launch geometry and sizes of a loaded model. */
 int amk_get_info(const amk_model* m, amk_info* info);
 
-/* Copies the codes and fp32 row scales the library uses for canonical tensor `tensor_index`
- * (a quantized projection, or, for AMK_W8A16, the lm_head index 2+9L / embed index 0 for a
- * tied model) back to host memory in canonical [rows][cols] order, one code per int8 (int4
- * codes unpacked, in [-7, 7]). codes_out: host int8 [rows*cols]; scales_out: host fp32 [rows].
+/* Copies the codes and scales the library uses for canonical tensor `tensor_index` (a quantized
+ * projection, or, for AMK_W8A16, the lm_head index 2+9L / embed index 0 for a tied model) back
+ * to host memory in canonical [rows][cols] order, one code per int8 (int4 codes unpacked, in
+ * [-7, 7]). codes_out: host int8 [rows*cols]; scales_out: host fp32 [rows] (row scales), or,
+ * for AMK_W4A16_G128, [rows][ceil(cols / 128)] (the fp16 group scales, widened exactly).
  * Errors: INVALID_ARG for a tensor that is not quantized (including the bf16 head of
- * AMK_W8A16_BF16_HEAD and AMK_W4A16); UNSUPPORTED for an AMK_BF16 model. */
+ * AMK_W8A16_BF16_HEAD, AMK_W4A16 and AMK_W4A16_G128); UNSUPPORTED for an AMK_BF16 model. */
 int amk_export_quantized(const amk_model* m, int32_t tensor_index, int8_t* codes_out,
                          float* scales_out);
 
@@ -242,6 +251,20 @@ int amk_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* cod
  * scales: host fp32 [rows]. Errors: INVALID_ARG for null pointers or non-positive sizes. */
 int amk_quantize_int4(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
                       float* scales);
+
+/* Host quantizer of AMK_W4A16_G128 (no GPU needed): the int4 rule applied to each group of 128
+ * consecutive columns of a row (a row whose length is not a multiple of 128 ends with a shorter
+ * group), with the scale held in IEEE half precision. Per group: amax = max |w|, s =
+ * fp16(fp32(amax / 7)) (IEEE fp32 division, then round to nearest even to half precision;
+ * values past 65504 saturate to 65504), q = clamp(round half to even(fp32(w / s)), -7, 7); s ==
+ * 0 gives q = 0. The pages give the int4 variant no format (gist.science explainer, Technical
+ * Summary > Key Contributions); per-group half-precision scales are the usual int4 weight-only
+ * layout, and at 128 columns they meet the pages' 2.42x weight-traffic figure most closely.
+ * w: host bf16 bit patterns [rows][cols]; codes: host int8 [rows][cols]; scales: host fp32
+ * [rows][ceil(cols / 128)] holding the half-precision values exactly. Errors: INVALID_ARG for
+ * null pointers or non-positive sizes. */
+int amk_quantize_int4_g128(const uint16_t* w, int64_t rows, int64_t cols, int8_t* codes,
+                           float* scales);
 
 /* Debug control: bound (in 100 MHz wall-clock ticks) on any single hand-off poll or barrier
  * wait; 0 restores the default (one second). A tiny bound makes steps fail cleanly with

@@ -12,7 +12,7 @@ import torch
 
 import decode_megakernel_cooperative_amd as D
 from decode_megakernel_cooperative_amd import amk as A
-from oracle.quant import quantize_rows_int4, quantize_rows_int8
+from oracle.quant import quantize_rows_int4, quantize_rows_int4_g128, quantize_rows_int8
 import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -66,6 +66,41 @@ def test_host_int4_quantizer_worked_rows():
         assert s[0] == np.float32(row["scale"])
 
 
+@pytest.mark.parametrize("rows,cols,std", [(96, 576, 0.02), (33, 4096, 0.02), (7, 1536, 0.5), (64, 2080, 3.0),
+                                           (5, 200, 1e-4), (3, 128, 2e5)])
+def test_host_int4_g128_quantizer_bit_exact_vs_oracle(rows, cols, std):
+    # includes a ragged last group (576, 2080, 200 columns), half-precision subnormal scales
+    # (std 1e-4: amax / 7 below 2^-14) and saturated ones (std 2e5: amax / 7 above 65504)
+    rng = np.random.default_rng(rows * cols + 5)
+    w = rng.standard_normal((rows, cols)) * std
+    w[0, :128] = 0.0  # an all-zero group
+    w = _bits(w)
+    c1, s1 = D.amk_quantize_int4_g128(w)
+    c2, s2 = quantize_rows_int4_g128(w)
+    assert s1.shape == (rows, (cols + 127) // 128)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.all(s1[0, 0] == 0) and np.all(c1[0, :128] == 0)
+    if std == 1e-4:
+        assert np.any((s1 > 0) & (s1 < 2.0 ** -14))
+    if std == 2e5:
+        assert np.any(s1 == np.float32(65504.0))
+
+
+def test_host_int4_g128_quantizer_worked_rows():
+    d = json.load(open(os.path.join(ROOT, "tests", "golden", "quant4g_tie_rows.json")))
+    for row in d["rows"]:
+        w = np.zeros(d["cols"], np.float32)
+        for k, v in row["nonzero_float"].items():
+            w[int(k)] = v
+        c, s = D.amk_quantize_int4_g128(_bits(w[None]))
+        want = np.zeros(d["cols"], np.int8)
+        for k, v in row["codes_nonzero"].items():
+            want[int(k)] = v
+        assert np.array_equal(c[0], want), row["why"]
+        assert np.array_equal(s[0], np.array(row["scales"], np.float32)), row["why"]
+
+
 def test_host_quantizer_bf16_shapes_of_real_models():
     # every (rows, cols) shape a W8A16 model of the measured workloads quantizes, on a few rows
     for shape in (W.SMOLLM2_135M, W.LLAMA32_1B, W.LLAMA3_8B):
@@ -111,10 +146,12 @@ def test_argument_validation_without_gpu():
     assert lib.amk_validate_config(ctypes.byref(cfg), 0) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_quantize_int8(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
     assert lib.amk_quantize_int4(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
+    assert lib.amk_quantize_int4_g128(None, 1, 1, None, None) == A.AMK_ERR_INVALID_ARG
     # W4A16 rows must hold whole 16-byte lane loads: 32-column multiples
-    bad = D.make_config(W.SMOLLM2_135M, 32, D.AMK_W4A16)
-    bad.ffn = 1552
-    assert lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h)) == A.AMK_ERR_UNSUPPORTED
+    for fmt in (D.AMK_W4A16, D.AMK_W4A16_G128):
+        bad = D.make_config(W.SMOLLM2_135M, 32, fmt)
+        bad.ffn = 1552
+        assert lib.amk_load_weights(ctypes.byref(bad), ptrs, 3, ctypes.byref(h)) == A.AMK_ERR_UNSUPPORTED
     assert "invalid argument" in D.amk_status_string(A.AMK_ERR_INVALID_ARG)
 
 

@@ -17,7 +17,8 @@ SHAPE = W.ModelShape("hf-hd128-gqa4-scaled", 512, 3, 8, 2, 128, 1376, 1000, Fals
                      rope_scaling=(8.0, 1.0, 4.0, 8192))
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16], ids=["bf16", "w8a16", "w4a16"])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128],
+                         ids=["bf16", "w8a16", "w4a16", "w4a16-g128"])
 def test_checkpoint_decode_matches_oracle(tmp_path, fmt):
     ws = W.gen_weights(SHAPE, seed0=12)
     write_checkpoint(str(tmp_path), SHAPE, ws, shards=2)

@@ -87,10 +87,12 @@ def _chain(dec, tok0, pos0, n, stream=None):
     return toks, lgs
 
 
-def test_greedy_w4a16_chain_follows_the_oracle():
-    """A device chain on the W4A16 format (int4 projections, bf16 lm_head): every written token
-    is the argmax of its own logits, and the chain is valid against the oracle replaying it."""
-    dec, orc, kv = build(SHAPE, D.AMK_W4A16, 40, 16, seed0=8)
+@pytest.mark.parametrize("fmt", [D.AMK_W4A16, D.AMK_W4A16_G128], ids=["w4a16", "w4a16-g128"])
+def test_greedy_w4a16_chain_follows_the_oracle(fmt):
+    """A device chain on the int4 formats (int4 projections with row or group scales, bf16
+    lm_head): every written token is the argmax of its own logits, and the chain is valid
+    against the oracle replaying it."""
+    dec, orc, kv = build(SHAPE, fmt, 40, 16, seed0=8)
     tok0 = W.gen_tokens(SHAPE, 1, seed0=8)[0]
     toks, lgs = _chain(dec, tok0, 16, 12)
     torch.cuda.synchronize()
@@ -104,7 +106,7 @@ def test_greedy_w4a16_chain_follows_the_oracle():
         if top2_margin(o) > MARGIN:
             assert int(toks[i + 1]) == int(np.argmax(o)), i
             checked += 1
-    log(f"  w4a16 chain: {checked} of 12 steps above the margin")
+    log(f"  fmt {fmt} chain: {checked} of 12 steps above the margin")
     dec.close()
 
 

@@ -10,7 +10,7 @@ import torch
 
 import decode_megakernel_cooperative_amd as D
 import workloads as W
-from oracle.quant import quantize_rows_int4, quantize_rows_int8
+from oracle.quant import quantize_rows_int4, quantize_rows_int4_g128, quantize_rows_int8
 from gpu_harness import LOGIT_TOL, build, log, run_teacher_forced
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +58,7 @@ def test_smollm2_w8a16_full_run_and_quantized_bytes():
     dec.close()
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128])
 def test_hd128_gqa4_prefilled_multi_split(fmt):
     """A small head_dim-128, 4-queries-per-kv-head model with a 300-position prefilled cache, so
     attention runs several KV splits with a ragged last split, and ragged GEMV rows (ffn 1376
@@ -97,7 +97,7 @@ def test_long_split_current_position_late_in_unit(fmt):
     dec.close()
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128])
 @pytest.mark.parametrize("which", ["hd128-g8", "hd64-g6"])
 def test_large_query_groups(which, fmt):
     """More than 4 query heads per kv head (the kernel variant that holds 8 heads per K/V load):
@@ -164,24 +164,32 @@ def test_w8a16_with_bf16_head(which):
     dec.close()
 
 
-@pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied"])
-def test_w4a16_parity(which):
-    """Int4 per-row projections (four bits per code) with the lm_head kept bf16: every
-    projection's codes and scales bit-exact against the oracle's quantizer, then the logit and
-    greedy gates over prompt and greedy steps (multi-split attention for the prefilled shape)."""
+@pytest.mark.parametrize("fmt", [D.AMK_W4A16, D.AMK_W4A16_G128])
+@pytest.mark.parametrize("which", ["smollm2-tied", "hd128-untied", "wide-ragged"])
+def test_w4a16_parity(which, fmt):
+    """Int4 projections (four bits per code; one scale per row, or an fp16 scale per row and 128
+    columns) with the lm_head kept bf16: every projection's codes and scales bit-exact against
+    the oracle's quantizer, then the per-stage checks and the logit and greedy gates over prompt
+    and greedy steps (multi-split attention for the prefilled shapes). The wide shape has rows of
+    2560 and 4416 columns: several 2048-column chunks per row, ragged last chunks and a ragged
+    last group (4416 = 34.5 groups)."""
     if which == "smollm2-tied":
         shape, ctx, pre, n_prompt, n_greedy = W.SMOLLM2_135M, 48, 0, 16, 24
-    else:
+    elif which == "hd128-untied":
         shape, ctx, pre, n_prompt, n_greedy = (W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False,
                                                             500000.0), 340, 300, 4, 12)
-    dec, orc, kv = build(shape, W.FMT_W4A16, ctx, pre, seed0=13)
+    else:
+        shape, ctx, pre, n_prompt, n_greedy = (W.ModelShape("wide-ragged", 2560, 2, 20, 5, 128, 4416, 1000, False,
+                                                            500000.0), 140, 100, 4, 8)
+    grouped = fmt == D.AMK_W4A16_G128
+    dec, orc, kv = build(shape, fmt, ctx, pre, seed0=13)
     ws = W.gen_weights(shape, 13)
     checked = 0
     for i, (name, dims, kind) in enumerate(W.tensor_specs(shape)):
         if kind != "matrix" or i == 0 or (not shape.tied and i == 2 + 9 * shape.n_layers):
             continue
-        codes, scales = D.amk_export_quantized(dec.model, i, dims[0], dims[1])
-        c_ref, s_ref = quantize_rows_int4(W.bf16_bits(ws[i]))
+        codes, scales = D.amk_export_quantized(dec.model, i, dims[0], dims[1], grouped=grouped)
+        c_ref, s_ref = (quantize_rows_int4_g128 if grouped else quantize_rows_int4)(W.bf16_bits(ws[i]))
         assert np.array_equal(codes, c_ref), name
         assert np.array_equal(scales.view(np.uint32), s_ref.view(np.uint32)), name
         checked += 1
@@ -191,8 +199,9 @@ def test_w4a16_parity(which):
         D.amk_export_quantized(dec.model, lm_idx, shape.vocab, shape.hidden)
     del ws
     toks = W.gen_tokens(shape, n_prompt, seed0=13)
-    res = run_teacher_forced(dec, orc, kv, shape, pre, toks, n_greedy, check_kv=True)
-    _assert_gates(res, f"w4a16 {which}")
+    res = run_teacher_forced(dec, orc, kv, shape, pre, toks, n_greedy, check_kv=True,
+                             stage_steps=(0, n_prompt + n_greedy - 1))
+    _assert_gates(res, f"{'w4a16-g128' if grouped else 'w4a16'} {which}")
     dec.close()
 
 
