@@ -131,6 +131,32 @@ def blas_info() -> dict:
     return {"vendor": "unknown", "threads": os.cpu_count() or 1, "version": None}
 
 
+def stage_trace(torch, D, dec, info, shape, tokens, pos0, n, stream) -> None:
+    """Per-stage times of n steps from the kernel's own per-block stamps (amk_set_trace), as a
+    table on stderr: per stage, the mean over blocks and the slowest block, averaged over the
+    layers after the first and over the steps."""
+    from decode_megakernel_cooperative_amd import trace as T
+    ne = T.events_per_block(shape.n_layers)
+    tr = torch.zeros((info.grid_blocks, ne), dtype=torch.int64, device=dec.device)
+    res = []
+    for i in range(n):
+        D.amk_set_trace(dec.model, tr, ne)
+        dec.step(tokens[i], pos0 + i, stream=stream)
+        torch.cuda.synchronize()
+        dec.sync()
+        res.append(T.summarize(tr.cpu().numpy(), shape.n_layers))
+    D.amk_set_trace(dec.model, None, 0)
+    log(f"[bench] stage trace: {n} steps at positions {pos0}..{pos0 + n - 1}, us")
+    log("| stage | mean over blocks | slowest block |")
+    log("|---|---|---|")
+    for name in T.STAGES:
+        log(f"| {name} | {np.mean([r[name]['mean_us'] for r in res]):.2f} | "
+            f"{np.mean([r[name]['max_over_blocks_us'] for r in res]):.2f} |")
+    log(f"| layer (sum of stage means) | {np.mean([r['layer_us'] for r in res]):.2f} | |")
+    log(f"| final norm + lm_head | {np.mean([r['lm_head_us'] for r in res]):.2f} | |")
+    log(f"| step (first stamp to last) | {np.mean([r['total_us'] for r in res]):.2f} | |")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +167,9 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle steps timed for the cpu baseline")
     ap.add_argument("--repeats", type=int, default=5,
                     help="times the K-step region is timed; value is the median (min and max reported)")
+    ap.add_argument("--stage-trace", type=int, default=0, metavar="N",
+                    help="after the timed region, run N more steps with per-block stage stamps "
+                         "(amk_set_trace) and print the per-stage summary to stderr")
     ap.add_argument("--greedy", action="store_true",
                     help="time device-resident greedy steps: each launch reads the token the previous "
                          "one wrote (amk_decode_step_greedy), no host involvement between launches")
@@ -218,6 +247,8 @@ def main() -> int:
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
     read_peak = measured_read_gbps(torch, dev)
     log(f"[bench] vendor bf16 GEMV (torch.mv) streams {read_peak:.0f} GB/s on this GPU")
+    if args.stage_trace > 0:
+        stage_trace(torch, D, dec, info, shape, tokens, pos0, min(args.stage_trace, steps), stream)
 
     if args.greedy:  # the oracle follows the tokens the device chain chose
         tokens = [int(t) for t in tok_dev.cpu().tolist()]

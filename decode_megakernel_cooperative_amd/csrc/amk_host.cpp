@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -710,8 +711,15 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   if (use_static) {
     k.tag0 = 1;
   } else {
+    // tags are compared for equality, so a wrap of the 32-bit counter would only matter where a
+    // launch's tag reached 0, the tag of a cleared word; restart from a cleared state well before
+    const uint32_t per_launch = static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
+    if (m->tag0 > UINT32_MAX - 2 * per_launch) {
+      const int rc = enqueue_reset(m, stream);
+      if (rc) return rc;
+    }
     k.tag0 = m->tag0;
-    m->tag0 += static_cast<uint32_t>(amk::kTagsPerLayer * m->cfg.n_layers + 1);
+    m->tag0 += per_launch;
   }
   void* args[] = {&k};
   HIP_TRY(hipLaunchCooperativeKernel(m->kernel, dim3(m->grid), dim3(amk::kThreads), args,
