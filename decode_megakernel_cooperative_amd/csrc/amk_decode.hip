@@ -941,38 +941,62 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
 // split-KV GQA attention
 // ------------------------------------------------------------------------------------------
 
-template <int GMAX>
-struct AttnRegs {
-  static constexpr int U = GMAX > 4 ? 2 : 4;  // position groups per wave per pipeline step
-  i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
+// Two forms of the stage. At head_dim 64 a unit runs on the matrix cores (below); at head_dim
+// 128 on the VALU, one position per row of 16 lanes (further below). Measured: the matrix-core
+// form makes Llama-3.2-1B and SmolLM2 steps 6-7% faster (its merge covers 8 wave results instead
+// of 64 row states), and Llama-3-8B steps 0.5% (4096 positions) and 3.4% (32768) slower (the V
+// tile's transpose through LDS costs more at head_dim 128 than the 32 row states it saves).
+//
+// Matrix-core form. A unit (kv head g, split j) covers positions [t0, t1) in tiles of kAttnTile =
+// 16 positions; wave w takes tiles w, w + 8, w + 16, ... For a tile, a wave forms the scores of the G heads
+// with bf16 matrix-core products (S^T = Q K^T: q, in base-2 units, split into a bf16 high and low
+// part, so it keeps 16 significant bits; K is bf16), updates each head's online softmax, and adds
+// P V the same way (P split into high and low parts, V bf16). Every product is exact in fp32 and
+// the sums are fp32. The waves' (max, sum, values) then merge through LDS into the unit's partial.
+//
+// MFMA operand layouts used (v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16): lane l
+// holds A[l % 16][k] and B[k][l % 16] for the k of its k block (8 (l / 16) .. + 7, or
+// 4 (l / 16) .. + 3), and the result D[4 (l / 16) + r][l % 16] in element r.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// One tile's K and V in the lane layout of the B operand of S^T = Q K^T: lane l holds position
+// l % 16 of the tile, dims c * 32 + 8 (l / 16) .. + 7 of chunk c.
+template <int HD>
+struct AttnTile {
+  i32x4 k[HD / 32], v[HD / 32];
+};
+template <int HD>
+struct AttnTileRegs {
+  AttnTile<HD> a, b;  // two tiles in flight per wave
 };
 
 // Running maxima start at a finite floor below every score, so the softmax weights need no
-// special case: exp2(-inf - m) and exp2(floor - m) are both 0 for any score m, and a row that has
-// seen no position keeps weight 0.
+// special case: exp2(-inf - m) and exp2(floor - m) are both 0 for any score m, and a wave (or,
+// in the VALU form, a row) that has seen no position keeps weight 0 in the merge.
 constexpr float kScoreFloor = -1.0e30f;
 
-// LDS of the attention stage, in floats: every row's softmax state (a row is the LPP lanes that
-// hold one position of a wave load: [R][GMAX][RS] = values, running max, running sum, merge
-// weight, pad), then each head's block max and sum, then q of the G heads and K/V(pos).
+// LDS of the matrix-core form (byte offsets): per wave a V tile [16][2 HD + 8 bytes], a P tile
+// [GMAX][16] fp32 and a result row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float
+// offset kQ) q of the G heads [G][HD] fp32 and K/V(pos) [2][HD] bf16. Matches attn_lds_bytes.
 template <int HD, int GMAX>
-struct AttnLds {
-  static constexpr int PPW = 64 / (HD / 8);
-  static constexpr int R = kWaves * PPW;
-  static constexpr int RS = HD + 4;
-  static constexpr int kHeads = R * GMAX * RS;
-  static constexpr int kQ = kHeads + 4 * GMAX;
+struct AttnTileLds {
+  static constexpr int kVStride = 2 * HD + 8;  // padded: the 4 position groups of a read hit other banks
+  static constexpr int kRStride = HD + 4;
+  static constexpr int kV = 0;
+  static constexpr int kP = kV + kWaves * kAttnTile * kVStride;
+  static constexpr int kRes = kP + kWaves * GMAX * kAttnTile * 4;
+  static constexpr int kQ = (kRes + kWaves * GMAX * kRStride * 4) / 4;
 };
 
 // Split-KV plan of this step: block u < nkv * S owns kv head g = u / S and positions
 // [j*T, min((j+1)*T, pos+1)) with j = u % S.
 struct AttnUnit {
-  int g, j, t0, t1, ngroups;
+  int g, j, t0, t1, ntiles, ngroups;  // ntiles: matrix-core tiles; ngroups: groups of the VALU form
   bool active;
 };
 template <int HD>
 __device__ __forceinline__ AttnUnit attn_unit(const KParams& p) {
-  constexpr int PPW = 64 / (HD / 8);
   AttnUnit a;
   const int S = p.S > 0 ? p.S : 1;
   const int u = blockIdx.x;
@@ -981,15 +1005,264 @@ __device__ __forceinline__ AttnUnit attn_unit(const KParams& p) {
   a.j = u - a.g * S;
   a.t0 = a.j * p.T;
   a.t1 = min(a.t0 + p.T, p.pos + 1);
+  a.ntiles = a.active ? (a.t1 - a.t0 + kAttnTile - 1) / kAttnTile : 0;
+  constexpr int PPW = 64 / (HD / 8);  // positions per wave load of the VALU form
   a.ngroups = a.active ? (a.t1 - a.t0 + PPW - 1) / PPW : 0;
   return a;
 }
+
+// buffer resource over the [max_ctx][HD] bf16 K (kv = 0) or V (kv = 1) block of (layer, kv head)
+template <int HD>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const KParams& p, int layer, int kv, int g) {
+  const uint16_t* base = p.kv + ((static_cast<size_t>(layer * 2 + kv) * p.nkv + g) * p.max_ctx) * HD;
+  return make_rsrc(base, static_cast<uint32_t>(p.max_ctx) * HD * 2);
+}
+
+// K/V loads of tile `tile` of the unit; positions past the unit (or tiles past the last) read
+// zeros. The current position's slot may still be in flight from another block's QKV stage; the
+// unit that holds pos replaces it with the copy that arrived with q.
+template <int HD>
+__device__ __forceinline__ void attn_tile_load(const AttnUnit& a, __amdgpu_buffer_rsrc_t kr,
+                                               __amdgpu_buffer_rsrc_t vr, int tile, AttnTile<HD>& T) {
+  const int lane = __lane_id();
+  const int t = a.t0 + tile * kAttnTile + (lane & 15);
+  const bool v = tile < a.ntiles && t < a.t1;
+  const int base = t * (HD * 2) + (lane >> 4) * 16;
+#pragma unroll
+  for (int c = 0; c < HD / 32; ++c) {
+    const int voff = v ? base + c * 64 : kOOB;
+    T.k[c] = ldbuf(kr, voff, 0);
+    T.v[c] = ldbuf(vr, voff, 0);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void attention_prefetch_tiles(const KParams& p, int layer, AttnTileRegs<HD>& R) {
+  const int wave = wave_id();
+  const AttnUnit a = attn_unit<HD>(p);
+  const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, a.g), vr = kv_rsrc<HD>(p, layer, 1, a.g);
+  attn_tile_load<HD>(a, kr, vr, wave, R.a);
+  attn_tile_load<HD>(a, kr, vr, wave + kWaves, R.b);
+}
+
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_stage_tiles(const KParams& p, int layer, float* smem, AttnTileRegs<HD>& R) {
+  using Lds = AttnTileLds<HD, GMAX>;
+  constexpr int NC = HD / 32;  // 32-dim chunks of the score product
+  constexpr int NV = HD / 16;  // 16-dim chunks of the value product
+  const float NEG_INF = -__builtin_inff();
+  const int S = p.S;
+  const int G = p.nq / p.nkv;
+  const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
+  const int col = lane & 15, kb = lane >> 4;  // the lane's MFMA column and k block
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  uint8_t* vt = lds + Lds::kV + wave * kAttnTile * Lds::kVStride;
+  float* pt = reinterpret_cast<float*>(lds + Lds::kP) + wave * GMAX * kAttnTile;
+  float* res = reinterpret_cast<float*>(lds + Lds::kRes);
+  const float* qs = smem + Lds::kQ;
+  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(qs + G * HD);  // K(pos) [HD], V(pos) [HD]
+  const AttnUnit a = attn_unit<HD>(p);
+  const int g = a.g, j = a.j;
+
+  if (a.active) {
+    // q as the A operand (lane l: head l % 16, dims c * 32 + 8 (l / 16) ..), in base-2 units (so
+    // every softmax weight is one exp2), split into bf16 high and low parts; heads past G are 0
+    const float qscale = p.attn_scale * 1.4426950408889634f;
+    bf16x8_t qh[NC], ql[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const f32x4 q0 = col < G ? *reinterpret_cast<const f32x4*>(qs + col * HD + c * 32 + kb * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 q1 = col < G ? *reinterpret_cast<const f32x4*>(qs + col * HD + c * 32 + kb * 8 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = (e < 4 ? q0[e & 3] : q1[e & 3]) * qscale;
+        const __bf16 hi = static_cast<__bf16>(q);
+        qh[c][e] = hi;
+        ql[c][e] = static_cast<__bf16>(q - static_cast<float>(hi));
+      }
+    }
+    // per head 4 kb + r (element r of the result rows this lane holds): running max (uniform over
+    // the 16 lanes of the row), this lane's share of the running sum, and the values
+    float mrun[4], lrun[4];
+    f32x4 o[NV];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mrun[r] = kScoreFloor;
+      lrun[r] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t0 = a.t0, t1 = a.t1, ntiles = a.ntiles;
+    const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, g), vr = kv_rsrc<HD>(p, layer, 1, g);
+    const int ipos = (t0 <= p.pos && p.pos < t1) ? (p.pos - t0) / kAttnTile : -1;  // uniform
+    const int cpos = (p.pos - t0) % kAttnTile;
+
+    auto process = [&](int tile, AttnTile<HD>& T) {
+      if (tile == ipos) {  // uniform: the lane holding pos takes K/V(pos) from the hand-off
+        const bool here = col == cpos;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + c * 32 + kb * 8);
+          const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + c * 32 + kb * 8);
+          T.k[c] = here ? kl : T.k[c];
+          T.v[c] = here ? vl : T.v[c];
+        }
+      }
+      // scores: element r of lane l is head 4 (l / 16) + r at position l % 16 of the tile
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8_t kc = __builtin_bit_cast(bf16x8_t, T.k[c]);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[c], kc, s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[c], kc, s, 0, 0, 0);
+      }
+      const bool valid = t0 + tile * kAttnTile + col < t1;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sv = valid ? s[r] : NEG_INF;
+        const float mnew = fmaxf(mrun[r], seg_max(sv, 16));
+        const float corr = __builtin_amdgcn_exp2f(mrun[r] - mnew);
+        pr[r] = __builtin_amdgcn_exp2f(sv - mnew);
+        lrun[r] = __builtin_fmaf(lrun[r], corr, pr[r]);
+        mrun[r] = mnew;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) o[n][r] *= corr;
+      }
+      // P through this wave's LDS tile [head][position] into the A operand of P V (lane l: head
+      // l % 16, positions 4 (l / 16) ..), and the V tile through LDS [position][dim] into the B
+      // operand (lane l: dim l % 16 of chunk n, positions 4 (l / 16) ..). A wave's LDS accesses
+      // complete in order, so no barrier is needed.
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * kb + r < GMAX) pt[(4 * kb + r) * kAttnTile + col] = pr[r];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        *reinterpret_cast<i32x4*>(vt + col * Lds::kVStride + (c * 32 + kb * 8) * 2) = T.v[c];
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(pt + min(col, GMAX - 1) * kAttnTile + kb * 4);
+      s16x4_t ah, al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 hi = static_cast<__bf16>(pv[e]);
+        ah[e] = __builtin_bit_cast(short, hi);
+        al[e] = __builtin_bit_cast(short, static_cast<__bf16>(pv[e] - static_cast<float>(hi)));
+      }
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        s16x4_t bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bv[e] = *reinterpret_cast<const short*>(vt + (kb * 4 + e) * Lds::kVStride + (n * 16 + col) * 2);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, o[n], 0, 0, 0);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, o[n], 0, 0, 0);
+      }
+    };
+
+    // two tiles in flight; loads past the unit read zeros, so the loop body has no branch
+    for (int tile = wave; tile < ntiles; tile += 2 * kWaves) {
+      process(tile, R.a);
+      attn_tile_load<HD>(a, kr, vr, tile + 2 * kWaves, R.a);
+      if (tile + kWaves < ntiles) process(tile + kWaves, R.b);  // uniform
+      attn_tile_load<HD>(a, kr, vr, tile + 3 * kWaves, R.b);
+    }
+
+    // this wave's result per head: values, max, and the sum over the row's 16 lanes (waves with
+    // no tile write max = floor and zeros, which the merge weighs 0)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * kb + r;
+      const float lsum = seg_sum(lrun[r], 16);
+      if (h < G) {
+        float* rw = res + (wave * GMAX + h) * Lds::kRStride;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) rw[n * 16 + col] = o[n][r];
+        if (col == 0) {
+          rw[HD] = mrun[r];
+          rw[HD + 1] = lsum;
+        }
+      }
+    }
+  }
+  wg_barrier();
+  if (!a.active) return;
+
+  // merge of the 8 waves: weights 2^(m_w - M) with M the largest wave max (finite: some wave holds
+  // the unit's first position). A partial is the weighted values, M and the weighted sum; a single
+  // split writes the normalised output as bf16 pairs.
+  const uint32_t tpart = tag_of(p, layer, kTagPart), to_tag = tag_of(p, layer, kTagO);
+  if (S == 1) {
+    for (int o2 = tid; o2 < G * HD / 2; o2 += kThreads) {
+      const int h = (2 * o2) / HD, d = 2 * o2 - h * HD;
+      float M = NEG_INF;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, res[(w * GMAX + h) * Lds::kRStride + HD]);
+      float A0 = 0.f, A1 = 0.f, Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* rw = res + (w * GMAX + h) * Lds::kRStride;
+        const float e = __builtin_amdgcn_exp2f(rw[HD] - M);
+        const float2 v = *reinterpret_cast<const float2*>(rw + d);
+        A0 = __builtin_fmaf(v.x, e, A0);
+        A1 = __builtin_fmaf(v.y, e, A1);
+        Ls = __builtin_fmaf(rw[HD + 1], e, Ls);
+      }
+      const float inv = 1.0f / Ls;
+      st_tag(p.to + ((g * G + h) * HD + d) / 2,
+             static_cast<uint32_t>(f32_to_bf16(A0 * inv)) | (static_cast<uint32_t>(f32_to_bf16(A1 * inv)) << 16),
+             to_tag);
+    }
+  } else {
+    // one output per thread, so a wave stores a run of consecutive words
+    for (int oi = tid; oi < G * HD; oi += kThreads) {
+      const int h = oi / HD, d = oi - h * HD;
+      float M = NEG_INF;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, res[(w * GMAX + h) * Lds::kRStride + HD]);
+      float A = 0.f, Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* rw = res + (w * GMAX + h) * Lds::kRStride;
+        const float e = __builtin_amdgcn_exp2f(rw[HD] - M);
+        A = __builtin_fmaf(rw[d], e, A);
+        Ls = __builtin_fmaf(rw[HD + 1], e, Ls);
+      }
+      uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
+      st_tag(dst + d, __float_as_uint(A), tpart);
+      if (d == 0) {
+        st_tag(dst + HD, __float_as_uint(M), tpart);
+        st_tag(dst + HD + 1, __float_as_uint(Ls), tpart);
+      }
+    }
+  }
+}
+
+// VALU form (head_dim 128). A row of hd/8 lanes holds one position (16 bytes per lane) of a wave
+// load; the G query heads of the kv head share every K/V load. Scores come from row sums by DPP
+// in base-2 units, each row keeps its own online softmax, and the rows' states merge in LDS.
+template <int GMAX>
+struct AttnRowRegs {
+  static constexpr int U = GMAX > 4 ? 2 : 4;  // position groups per wave per pipeline step
+  i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
+};
+
+
+// LDS of the attention stage, in floats: every row's softmax state (a row is the LPP lanes that
+// hold one position of a wave load: [R][GMAX][RS] = values, running max, running sum, merge
+// weight, pad), then each head's block max and sum, then q of the G heads and K/V(pos).
+template <int HD, int GMAX>
+struct AttnRowLds {
+  static constexpr int PPW = 64 / (HD / 8);
+  static constexpr int R = kWaves * PPW;
+  static constexpr int RS = HD + 4;
+  static constexpr int kHeads = R * GMAX * RS;
+  static constexpr int kQ = kHeads + 4 * GMAX;
+};
 
 // K/V loads of one pipeline step of a wave: U groups of PPW positions, one position per row
 // of LPP lanes. With skip_pos, the current position (written by this step's QKV stage,
 // possibly still in flight) is left out: the prefetch issued before q arrives uses that.
 template <int HD, int U>
-__device__ __forceinline__ void attn_load(const KParams& p, const AttnUnit& a, __amdgpu_buffer_rsrc_t kr_rs,
+__device__ __forceinline__ void attn_row_load(const KParams& p, const AttnUnit& a, __amdgpu_buffer_rsrc_t kr_rs,
                                           __amdgpu_buffer_rsrc_t vr_rs, int gbase, bool skip_pos, i32x4 (&kr)[U],
                                           i32x4 (&vr)[U]) {
   constexpr int LPP = HD / 8, PPW = 64 / LPP;
@@ -1006,27 +1279,20 @@ __device__ __forceinline__ void attn_load(const KParams& p, const AttnUnit& a, _
   }
 }
 
-// buffer resource over the [max_ctx][HD] bf16 K (kv = 0) or V (kv = 1) block of (layer, kv head)
-template <int HD>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const KParams& p, int layer, int kv, int g) {
-  const uint16_t* base = p.kv + ((static_cast<size_t>(layer * 2 + kv) * p.nkv + g) * p.max_ctx) * HD;
-  return make_rsrc(base, static_cast<uint32_t>(p.max_ctx) * HD * 2);
-}
-
 template <int HD, int GMAX>
-__device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, AttnRegs<GMAX>& R) {
-  constexpr int U = AttnRegs<GMAX>::U;
+__device__ __forceinline__ void attention_prefetch_rows(const KParams& p, int layer, AttnRowRegs<GMAX>& R) {
+  constexpr int U = AttnRowRegs<GMAX>::U;
   const int wave = wave_id();
   const AttnUnit a = attn_unit<HD>(p);
   const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, a.g), vr = kv_rsrc<HD>(p, layer, 1, a.g);
   // all lanes load (out-of-range groups read zeros), so R is written on every path
-  attn_load<HD, U>(p, a, kr, vr, wave, true, R.ka, R.va);
-  attn_load<HD, U>(p, a, kr, vr, wave + kWaves * U, true, R.kb, R.vb);
+  attn_row_load<HD, U>(p, a, kr, vr, wave, true, R.ka, R.va);
+  attn_row_load<HD, U>(p, a, kr, vr, wave + kWaves * U, true, R.kb, R.vb);
 }
 
 template <int HD, int GMAX>
-__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, AttnRegs<GMAX>& R) {
-  constexpr int kAttnU = AttnRegs<GMAX>::U;
+__device__ __forceinline__ void attention_stage_rows(const KParams& p, int layer, float* smem, AttnRowRegs<GMAX>& R) {
+  constexpr int kAttnU = AttnRowRegs<GMAX>::U;
   constexpr int LPP = HD / 8;     // lanes per position (8 bf16 = 16 bytes per lane)
   constexpr int PPW = 64 / LPP;   // positions per wave load
   const float NEG_INF = -__builtin_inff();
@@ -1034,7 +1300,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   const int G = p.nq / p.nkv;
   const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
   const int li = lane % LPP, ri = lane / LPP, d0 = li * 8;
-  using Lds = AttnLds<HD, GMAX>;
+  using Lds = AttnRowLds<HD, GMAX>;
   constexpr int NR = Lds::R, RS = Lds::RS;
   float* wp = smem;                   // row states [R][GMAX][RS]
   float* hs = smem + Lds::kHeads;     // per head: block max, block sum
@@ -1071,7 +1337,7 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       }
     };
     auto load = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
-      attn_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
+      attn_row_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
     };
 
     // scores are kept in base-2 units (q pre-scaled by log2(e) / sqrt(HD)), so every softmax
@@ -1271,6 +1537,24 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   }
 }
 
+
+// The form the kernel runs for a head_dim (see the measurements at the top of this section).
+template <int HD> constexpr bool kAttnTiles = HD == 64;
+template <int HD, int GMAX>
+using AttnRegs = std::conditional_t<kAttnTiles<HD>, AttnTileRegs<HD>, AttnRowRegs<GMAX>>;
+template <int HD, int GMAX>
+using AttnLds = std::conditional_t<kAttnTiles<HD>, AttnTileLds<HD, GMAX>, AttnRowLds<HD, GMAX>>;
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, AttnRegs<HD, GMAX>& R) {
+  if constexpr (kAttnTiles<HD>) attention_prefetch_tiles<HD>(p, layer, R);
+  else attention_prefetch_rows<HD, GMAX>(p, layer, R);
+}
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, AttnRegs<HD, GMAX>& R) {
+  if constexpr (kAttnTiles<HD>) attention_stage_tiles<HD, GMAX>(p, layer, smem, R);
+  else attention_stage_rows<HD, GMAX>(p, layer, smem, R);
+}
+
 // The blocks of kv head g each merge one slice of the head's G * HD outputs over its S splits
 // (log-sum-exp weights) and write it as tagged bf16 pairs. Thread t holds split t % SP of output
 // word w0 + t / SP (plus 512 / SP in a second round, run when the slice reaches it); SP = S rounded
@@ -1461,7 +1745,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;
   GemvRegs R;
-  AttnRegs<GMAX> AR;
+  AttnRegs<HD, GMAX> AR;
   bool ok = true;
   // end of a hand-off: the next stage's input is in LDS, or every thread leaves
   auto handoff_done = [&]() -> bool {

@@ -391,11 +391,9 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
   auto pad = [&](int64_t k) { return (k + cw - 1) / cw * cw; };
   const int64_t xs_f = std::max({pad(H), pad(QD), pad(F)});
   {
-    // attention: every row's softmax state (a row: the lanes holding one position of a wave's
-    // load, 512 / hd rows per wave), each head's max and sum, then q of the G heads and K/V(pos)
-    const int64_t rows = static_cast<int64_t>(amk::kWaves) * (512 / hd);
-    const int64_t attn_f = rows * m->gmax * (hd + 4) + 4 * m->gmax + G * hd + hd;
-    m->lds_bytes = static_cast<int>(4 * std::max(xs_f, attn_f));
+    // the GEMV input vector, or the attention stage's tiles, results, q and K/V(pos)
+    const int64_t attn_b = amk::attn_lds_bytes(static_cast<int>(hd), m->gmax, G);
+    m->lds_bytes = static_cast<int>(std::max(4 * xs_f, attn_b));
     m->kernel = amk_kernel_handle(static_cast<int>(hd), kfmt, m->gmax);
   }
   if (m->lds_bytes > 160 * 1024) { delete m; return fail(AMK_ERR_UNSUPPORTED, "LDS need exceeds 160 KB"); }
@@ -693,9 +691,10 @@ int launch_step(amk_model* m, int32_t token, const int32_t* token_dev, int32_t p
   k.pos = pos;
   const int ctx = pos + 1;
   // split-KV plan: at most s_cap splits per kv head (one attention unit per block), at least
-  // 16 positions per split. The wave kernel keeps a context that one block covers in a single
-  // pipeline step (8 waves x U groups x 512 / head_dim positions) in one split, which then writes
-  // the attention output itself, with no merge hand-off.
+  // 16 positions per split. A context of at most tstep positions (128 at head_dim 128, 256 at
+  // head_dim 64, half that with more than 4 query heads per kv head: one or two 16-position tiles
+  // per wave) runs as one split per kv head, which writes the attention output itself, with no
+  // merge hand-off.
   const int tstep = amk::kWaves * (m->gmax > 4 ? 2 : 4) * (512 / m->cfg.head_dim);
   int T = std::max(16, (ctx + m->s_cap - 1) / m->s_cap);
   if (ctx <= tstep) T = tstep;

@@ -121,8 +121,8 @@ def test_large_query_groups(which, fmt):
 
 @pytest.mark.parametrize("which", ["hd128", "hd64"])
 def test_single_split_boundary(which):
-    """A context that one block covers in a single pipeline step (8 waves x 4 groups x 512 /
-    head_dim positions: 128 at head_dim 128, 256 at head_dim 64) runs one split per kv head,
+    """A context of at most 128 positions at head_dim 128 (256 at head_dim 64: one or two
+    16-position tiles per wave of one block) runs one split per kv head,
     which writes the attention output without the split merge; one position more switches to
     many splits. Steps on both sides of the switch, and the current position at the last slot of
     the single split."""
