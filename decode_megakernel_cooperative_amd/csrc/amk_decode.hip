@@ -941,18 +941,16 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
 // split-KV GQA attention
 // ------------------------------------------------------------------------------------------
 
-// Two forms of the stage. At head_dim 64 a unit runs on the matrix cores (below); at head_dim
-// 128 on the VALU, one position per row of 16 lanes (further below). Measured: the matrix-core
-// form makes Llama-3.2-1B and SmolLM2 steps 6-7% faster (its merge covers 8 wave results instead
-// of 64 row states), and Llama-3-8B steps 0.5% (4096 positions) and 3.4% (32768) slower (the V
-// tile's transpose through LDS costs more at head_dim 128 than the 32 row states it saves).
-//
-// Matrix-core form. A unit (kv head g, split j) covers positions [t0, t1) in tiles of kAttnTile =
-// 16 positions; wave w takes tiles w, w + 8, w + 16, ... For a tile, a wave forms the scores of the G heads
+// A unit (kv head g, split j) covers positions [t0, t1) in tiles of kAttnTile = 16 positions;
+// wave w takes tiles w, w + 8, w + 16, ... For a tile, a wave forms the scores of the G heads
 // with bf16 matrix-core products (S^T = Q K^T: q, in base-2 units, split into a bf16 high and low
 // part, so it keeps 16 significant bits; K is bf16), updates each head's online softmax, and adds
 // P V the same way (P split into high and low parts, V bf16). Every product is exact in fp32 and
 // the sums are fp32. The waves' (max, sum, values) then merge through LDS into the unit's partial.
+//
+// K and V are loaded in whole position rows (hd / 8 lanes of 16 bytes per row, so one load
+// instruction reads 64 / (hd / 8) complete rows) and reach the MFMA operand layouts through a
+// per-wave LDS tile: K with plain 16-byte reads, V with the transposing ds_read_b64_tr_b16.
 //
 // MFMA operand layouts used (v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16): lane l
 // holds A[l % 16][k] and B[k][l % 16] for the k of its k block (8 (l / 16) .. + 7, or
@@ -960,30 +958,31 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// One tile's K and V in the lane layout of the B operand of S^T = Q K^T: lane l holds position
-// l % 16 of the tile, dims c * 32 + 8 (l / 16) .. + 7 of chunk c.
+// One tile's K and V as loaded: register m of lane l holds the 16 bytes at byte (l % (hd / 8)) * 16
+// of position row (64 / (hd / 8)) * m + l / (hd / 8) of the tile.
 template <int HD>
 struct AttnTile {
   i32x4 k[HD / 32], v[HD / 32];
 };
 template <int HD>
-struct AttnTileRegs {
+struct AttnRegs {
   AttnTile<HD> a, b;  // two tiles in flight per wave
 };
 
 // Running maxima start at a finite floor below every score, so the softmax weights need no
-// special case: exp2(-inf - m) and exp2(floor - m) are both 0 for any score m, and a wave (or,
-// in the VALU form, a row) that has seen no position keeps weight 0 in the merge.
+// special case: exp2(-inf - m) and exp2(floor - m) are both 0 for any score m, and a wave that
+// has seen no position keeps weight 0 in the merge.
 constexpr float kScoreFloor = -1.0e30f;
 
-// LDS of the matrix-core form (byte offsets): per wave a V tile [16][2 HD + 8 bytes], a P tile
+// LDS of the stage (byte offsets): per wave a K and a V tile [16][2 HD + 32 bytes], a P tile
 // [GMAX][16] fp32 and a result row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float
 // offset kQ) q of the G heads [G][HD] fp32 and K/V(pos) [2][HD] bf16. Matches attn_lds_bytes.
 template <int HD, int GMAX>
-struct AttnTileLds {
-  static constexpr int kVStride = 2 * HD + 8;  // padded: the 4 position groups of a read hit other banks
+struct AttnLds {
+  static constexpr int kVStride = 2 * HD + 32;  // padded: the 16 rows of a transposed read spread over the banks
   static constexpr int kRStride = HD + 4;
-  static constexpr int kV = 0;
+  static constexpr int kK = 0;
+  static constexpr int kV = kK + kWaves * kAttnTile * kVStride;
   static constexpr int kP = kV + kWaves * kAttnTile * kVStride;
   static constexpr int kRes = kP + kWaves * GMAX * kAttnTile * 4;
   static constexpr int kQ = (kRes + kWaves * GMAX * kRStride * 4) / 4;
@@ -992,7 +991,7 @@ struct AttnTileLds {
 // Split-KV plan of this step: block u < nkv * S owns kv head g = u / S and positions
 // [j*T, min((j+1)*T, pos+1)) with j = u % S.
 struct AttnUnit {
-  int g, j, t0, t1, ntiles, ngroups;  // ntiles: matrix-core tiles; ngroups: groups of the VALU form
+  int g, j, t0, t1, ntiles;
   bool active;
 };
 template <int HD>
@@ -1006,8 +1005,6 @@ __device__ __forceinline__ AttnUnit attn_unit(const KParams& p) {
   a.t0 = a.j * p.T;
   a.t1 = min(a.t0 + p.T, p.pos + 1);
   a.ntiles = a.active ? (a.t1 - a.t0 + kAttnTile - 1) / kAttnTile : 0;
-  constexpr int PPW = 64 / (HD / 8);  // positions per wave load of the VALU form
-  a.ngroups = a.active ? (a.t1 - a.t0 + PPW - 1) / PPW : 0;
   return a;
 }
 
@@ -1025,19 +1022,19 @@ template <int HD>
 __device__ __forceinline__ void attn_tile_load(const AttnUnit& a, __amdgpu_buffer_rsrc_t kr,
                                                __amdgpu_buffer_rsrc_t vr, int tile, AttnTile<HD>& T) {
   const int lane = __lane_id();
-  const int t = a.t0 + tile * kAttnTile + (lane & 15);
-  const bool v = tile < a.ntiles && t < a.t1;
-  const int base = t * (HD * 2) + (lane >> 4) * 16;
+  constexpr int LPP = HD / 8, PPI = 64 / LPP;  // lanes per position row, rows per load
 #pragma unroll
-  for (int c = 0; c < HD / 32; ++c) {
-    const int voff = v ? base + c * 64 : kOOB;
-    T.k[c] = ldbuf(kr, voff, 0);
-    T.v[c] = ldbuf(vr, voff, 0);
+  for (int m = 0; m < HD / 32; ++m) {
+    const int t = a.t0 + tile * kAttnTile + PPI * m + lane / LPP;
+    const bool v = tile < a.ntiles && t < a.t1;
+    const int voff = v ? t * (HD * 2) + (lane % LPP) * 16 : kOOB;
+    T.k[m] = ldbuf(kr, voff, 0);
+    T.v[m] = ldbuf(vr, voff, 0);
   }
 }
 
-template <int HD>
-__device__ __forceinline__ void attention_prefetch_tiles(const KParams& p, int layer, AttnTileRegs<HD>& R) {
+template <int HD, int GMAX>
+__device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, AttnRegs<HD>& R) {
   const int wave = wave_id();
   const AttnUnit a = attn_unit<HD>(p);
   const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, a.g), vr = kv_rsrc<HD>(p, layer, 1, a.g);
@@ -1046,8 +1043,8 @@ __device__ __forceinline__ void attention_prefetch_tiles(const KParams& p, int l
 }
 
 template <int HD, int GMAX>
-__device__ __forceinline__ void attention_stage_tiles(const KParams& p, int layer, float* smem, AttnTileRegs<HD>& R) {
-  using Lds = AttnTileLds<HD, GMAX>;
+__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, AttnRegs<HD>& R) {
+  using Lds = AttnLds<HD, GMAX>;
   constexpr int NC = HD / 32;  // 32-dim chunks of the score product
   constexpr int NV = HD / 16;  // 16-dim chunks of the value product
   const float NEG_INF = -__builtin_inff();
@@ -1057,6 +1054,8 @@ __device__ __forceinline__ void attention_stage_tiles(const KParams& p, int laye
   const int col = lane & 15, kb = lane >> 4;  // the lane's MFMA column and k block
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
   uint8_t* vt = lds + Lds::kV + wave * kAttnTile * Lds::kVStride;
+  uint8_t* kt = lds + Lds::kK + wave * kAttnTile * Lds::kVStride;
+  constexpr int LPP = HD / 8, PPI = 64 / LPP;
   float* pt = reinterpret_cast<float*>(lds + Lds::kP) + wave * GMAX * kAttnTile;
   float* res = reinterpret_cast<float*>(lds + Lds::kRes);
   const float* qs = smem + Lds::kQ;
@@ -1098,21 +1097,22 @@ __device__ __forceinline__ void attention_stage_tiles(const KParams& p, int laye
     const int cpos = (p.pos - t0) % kAttnTile;
 
     auto process = [&](int tile, AttnTile<HD>& T) {
-      if (tile == ipos) {  // uniform: the lane holding pos takes K/V(pos) from the hand-off
-        const bool here = col == cpos;
+      const int row = lane / LPP, cb = (lane % LPP) * 16;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + c * 32 + kb * 8);
-          const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + c * 32 + kb * 8);
-          T.k[c] = here ? kl : T.k[c];
-          T.v[c] = here ? vl : T.v[c];
-        }
+      for (int m = 0; m < NC; ++m) {
+        *reinterpret_cast<i32x4*>(kt + (PPI * m + row) * Lds::kVStride + cb) = T.k[m];
+        *reinterpret_cast<i32x4*>(vt + (PPI * m + row) * Lds::kVStride + cb) = T.v[m];
+      }
+      if (tile == ipos && lane < LPP) {  // K/V(pos) from the hand-off replace the cache's slot
+        *reinterpret_cast<i32x4*>(kt + cpos * Lds::kVStride + lane * 16) = *reinterpret_cast<const i32x4*>(kvp + lane * 8);
+        *reinterpret_cast<i32x4*>(vt + cpos * Lds::kVStride + lane * 16) =
+            *reinterpret_cast<const i32x4*>(kvp + HD + lane * 8);
       }
       // scores: element r of lane l is head 4 (l / 16) + r at position l % 16 of the tile
       f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8_t kc = __builtin_bit_cast(bf16x8_t, T.k[c]);
+        const bf16x8_t kc = *reinterpret_cast<const bf16x8_t*>(kt + col * Lds::kVStride + (c * 32 + kb * 8) * 2);
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[c], kc, s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[c], kc, s, 0, 0, 0);
       }
@@ -1136,9 +1136,6 @@ __device__ __forceinline__ void attention_stage_tiles(const KParams& p, int laye
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * kb + r < GMAX) pt[(4 * kb + r) * kAttnTile + col] = pr[r];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        *reinterpret_cast<i32x4*>(vt + col * Lds::kVStride + (c * 32 + kb * 8) * 2) = T.v[c];
       const f32x4 pv = *reinterpret_cast<const f32x4*>(pt + min(col, GMAX - 1) * kAttnTile + kb * 4);
       s16x4_t ah, al;
 #pragma unroll
@@ -1147,12 +1144,14 @@ __device__ __forceinline__ void attention_stage_tiles(const KParams& p, int laye
         ah[e] = __builtin_bit_cast(short, hi);
         al[e] = __builtin_bit_cast(short, static_cast<__bf16>(pv[e] - static_cast<float>(hi)));
       }
+      // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of the
+      // 8 bytes addressed by lanes 4 e + i / 4 (e = 0..3). Lane 4 e + c of k block kb addresses
+      // position 4 kb + e, dims n * 16 + 4 c .., so lane i gets V[4 kb + e][n * 16 + i].
+      const int vrow = (kb * 4 + (col >> 2)) * Lds::kVStride + 8 * (col & 3);
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        s16x4_t bv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bv[e] = *reinterpret_cast<const short*>(vt + (kb * 4 + e) * Lds::kVStride + (n * 16 + col) * 2);
+        const s16x4_t bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vt + vrow + n * 32));
         o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, o[n], 0, 0, 0);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, o[n], 0, 0, 0);
       }
@@ -1234,325 +1233,6 @@ __device__ __forceinline__ void attention_stage_tiles(const KParams& p, int laye
       }
     }
   }
-}
-
-// VALU form (head_dim 128). A row of hd/8 lanes holds one position (16 bytes per lane) of a wave
-// load; the G query heads of the kv head share every K/V load. Scores come from row sums by DPP
-// in base-2 units, each row keeps its own online softmax, and the rows' states merge in LDS.
-template <int GMAX>
-struct AttnRowRegs {
-  static constexpr int U = GMAX > 4 ? 2 : 4;  // position groups per wave per pipeline step
-  i32x4 ka[U], va[U], kb[U], vb[U];           // two pipeline buffers
-};
-
-
-// LDS of the attention stage, in floats: every row's softmax state (a row is the LPP lanes that
-// hold one position of a wave load: [R][GMAX][RS] = values, running max, running sum, merge
-// weight, pad), then each head's block max and sum, then q of the G heads and K/V(pos).
-template <int HD, int GMAX>
-struct AttnRowLds {
-  static constexpr int PPW = 64 / (HD / 8);
-  static constexpr int R = kWaves * PPW;
-  static constexpr int RS = HD + 4;
-  static constexpr int kHeads = R * GMAX * RS;
-  static constexpr int kQ = kHeads + 4 * GMAX;
-};
-
-// K/V loads of one pipeline step of a wave: U groups of PPW positions, one position per row
-// of LPP lanes. With skip_pos, the current position (written by this step's QKV stage,
-// possibly still in flight) is left out: the prefetch issued before q arrives uses that.
-template <int HD, int U>
-__device__ __forceinline__ void attn_row_load(const KParams& p, const AttnUnit& a, __amdgpu_buffer_rsrc_t kr_rs,
-                                          __amdgpu_buffer_rsrc_t vr_rs, int gbase, bool skip_pos, i32x4 (&kr)[U],
-                                          i32x4 (&vr)[U]) {
-  constexpr int LPP = HD / 8, PPW = 64 / LPP;
-  const int lane = __lane_id();
-  const int ri = lane / LPP, lo = (lane % LPP) * 16;
-#pragma unroll
-  for (int uu = 0; uu < U; ++uu) {
-    const int gg = gbase + uu * kWaves;
-    const int t = a.t0 + gg * PPW + ri;
-    const bool v = gg < a.ngroups && t < a.t1 && !(skip_pos && t == p.pos);
-    const int voff = v ? t * (HD * 2) + lo : kOOB;
-    kr[uu] = ldbuf(kr_rs, voff, 0);
-    vr[uu] = ldbuf(vr_rs, voff, 0);
-  }
-}
-
-template <int HD, int GMAX>
-__device__ __forceinline__ void attention_prefetch_rows(const KParams& p, int layer, AttnRowRegs<GMAX>& R) {
-  constexpr int U = AttnRowRegs<GMAX>::U;
-  const int wave = wave_id();
-  const AttnUnit a = attn_unit<HD>(p);
-  const __amdgpu_buffer_rsrc_t kr = kv_rsrc<HD>(p, layer, 0, a.g), vr = kv_rsrc<HD>(p, layer, 1, a.g);
-  // all lanes load (out-of-range groups read zeros), so R is written on every path
-  attn_row_load<HD, U>(p, a, kr, vr, wave, true, R.ka, R.va);
-  attn_row_load<HD, U>(p, a, kr, vr, wave + kWaves * U, true, R.kb, R.vb);
-}
-
-template <int HD, int GMAX>
-__device__ __forceinline__ void attention_stage_rows(const KParams& p, int layer, float* smem, AttnRowRegs<GMAX>& R) {
-  constexpr int kAttnU = AttnRowRegs<GMAX>::U;
-  constexpr int LPP = HD / 8;     // lanes per position (8 bf16 = 16 bytes per lane)
-  constexpr int PPW = 64 / LPP;   // positions per wave load
-  const float NEG_INF = -__builtin_inff();
-  const int S = p.S;
-  const int G = p.nq / p.nkv;
-  const int tid = opaque(threadIdx.x), lane = tid & 63, wave = wave_id();
-  const int li = lane % LPP, ri = lane / LPP, d0 = li * 8;
-  using Lds = AttnRowLds<HD, GMAX>;
-  constexpr int NR = Lds::R, RS = Lds::RS;
-  float* wp = smem;                   // row states [R][GMAX][RS]
-  float* hs = smem + Lds::kHeads;     // per head: block max, block sum
-  const float* qs = smem + Lds::kQ;   // q of the G heads [G][HD]
-  const uint16_t* kvp = reinterpret_cast<const uint16_t*>(qs + G * HD);  // K(pos) [HD], V(pos) [HD]
-  const AttnUnit a = attn_unit<HD>(p);
-  const int g = a.g, j = a.j;
-
-  if (a.active) {
-    const int t0 = a.t0, t1 = a.t1, ngroups = a.ngroups;
-    const __amdgpu_buffer_rsrc_t kb = kv_rsrc<HD>(p, layer, 0, g);
-    const __amdgpu_buffer_rsrc_t vb = kv_rsrc<HD>(p, layer, 1, g);
-    i32x4 (&KA)[kAttnU] = R.ka;
-    i32x4 (&VA)[kAttnU] = R.va;
-    i32x4 (&KB)[kAttnU] = R.kb;
-    i32x4 (&VB)[kAttnU] = R.vb;
-    const int step = kWaves * kAttnU;
-    // The current position's K/V are written by this step's QKV stage on another block: plain
-    // stores that need not be visible here yet. The unit that holds pos received them with q
-    // (LDS); whatever the cache load of that slot returned is replaced before use.
-    const int gpos = (t0 <= p.pos && p.pos < t1) ? (p.pos - t0) / PPW : -1;  // uniform
-    const int rpos = (p.pos - t0) % PPW;
-    auto patch_pos = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
-      const int dg = gpos - gbase;
-      if (dg >= 0 && dg < kAttnU * kWaves && dg % kWaves == 0) {  // uniform: at most once per unit
-        const i32x4 kl = *reinterpret_cast<const i32x4*>(kvp + li * 8);
-        const i32x4 vl = *reinterpret_cast<const i32x4*>(kvp + HD + li * 8);
-#pragma unroll
-        for (int uu = 0; uu < kAttnU; ++uu) {
-          const bool here = uu == dg / kWaves && ri == rpos;
-          kr[uu] = here ? kl : kr[uu];
-          vr[uu] = here ? vl : vr[uu];
-        }
-      }
-    };
-    auto load = [&](int gbase, i32x4 (&kr)[kAttnU], i32x4 (&vr)[kAttnU]) {
-      attn_row_load<HD, kAttnU>(p, a, kb, vb, gbase, false, kr, vr);
-    };
-
-    // scores are kept in base-2 units (q pre-scaled by log2(e) / sqrt(HD)), so every softmax
-    // weight is one exp2
-    const float qscale = p.attn_scale * 1.4426950408889634f;
-    float qv[GMAX][8];
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      if (h < G) {
-        const float* qp = qs + h * HD + d0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[h][i] = qp[i] * qscale;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[h][i] = 0.f;
-      }
-    }
-    float mr[GMAX], lr[GMAX], acc[GMAX][8];
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      mr[h] = kScoreFloor;
-      lr[h] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-    }
-
-    auto compute = [&](int gbase, const i32x4 (&kr)[kAttnU], const i32x4 (&vr)[kAttnU]) {
-      float s[kAttnU][GMAX];
-#pragma unroll
-      for (int uu = 0; uu < kAttnU; ++uu) {
-        const int gg = gbase + uu * kWaves;
-        const bool valid = gg < ngroups && (t0 + gg * PPW + ri) < t1;
-        if (gg >= ngroups) {  // uniform: no position of this group is in the unit
-#pragma unroll
-          for (int h = 0; h < GMAX; ++h) s[uu][h] = NEG_INF;
-          continue;
-        }
-        float kf[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          kf[2 * d] = bf_lo(kr[uu][d]);
-          kf[2 * d + 1] = bf_hi(kr[uu][d]);
-        }
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-          float dot = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dot = __builtin_fmaf(qv[h][i], kf[i], dot);
-          dot = group_sum<LPP>(dot);
-          s[uu][h] = valid ? dot : NEG_INF;
-        }
-      }
-      // online softmax: new running max, rescale, and this step's weights (all zero while a row
-      // has seen no position: its max stays -inf and its sums stay 0)
-      float pe[kAttnU][GMAX];
-#pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) continue;
-        float mnew = mr[h];
-#pragma unroll
-        for (int uu = 0; uu < kAttnU; ++uu) mnew = fmaxf(mnew, s[uu][h]);
-        const float corr = __builtin_amdgcn_exp2f(mr[h] - mnew);
-        lr[h] *= corr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= corr;
-#pragma unroll
-        for (int uu = 0; uu < kAttnU; ++uu) {
-          pe[uu][h] = __builtin_amdgcn_exp2f(s[uu][h] - mnew);
-          lr[h] += pe[uu][h];
-        }
-        mr[h] = mnew;
-      }
-      // values: each group's V converted once, shared by the G heads
-#pragma unroll
-      for (int uu = 0; uu < kAttnU; ++uu) {
-        if (gbase + uu * kWaves >= ngroups) continue;  // uniform
-        float vf[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          vf[2 * d] = bf_lo(vr[uu][d]);
-          vf[2 * d + 1] = bf_hi(vr[uu][d]);
-        }
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-          if (h >= G) continue;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pe[uu][h], vf[i], acc[h][i]);
-        }
-      }
-    };
-
-    // two buffers in flight; loads past the unit read zeros, so the loop body has no branch
-    for (int gb = wave; gb < ngroups; gb += 2 * step) {
-      patch_pos(gb, KA, VA);
-      compute(gb, KA, VA);
-      load(gb + 2 * step, KA, VA);
-      if (gb + step < ngroups) {  // uniform
-        patch_pos(gb + step, KB, VB);
-        compute(gb + step, KB, VB);
-      }
-      load(gb + 3 * step, KB, VB);
-    }
-
-    // every row's state into LDS (each row saw its own positions); rows that saw none hold
-    // max -inf and zero sums
-    float* row = wp + (wave * Lds::PPW + ri) * GMAX * RS;
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      if (h >= G) continue;
-      float* dst = row + h * RS + d0;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-      if (li == 0) {
-        row[h * RS + HD] = mr[h];
-        row[h * RS + HD + 1] = lr[h];
-      }
-    }
-  }
-  wg_barrier();
-  if (!a.active) return;
-
-  // wave h < G: the head's block max M over the R rows, each row's weight 2^(m - M) and the
-  // block sum of the rows' sums under those weights
-  if (wave < G) {
-    const int h = wave;
-    float* rp = wp + (min(lane, NR - 1) * GMAX + h) * RS;
-    const float m = lane < NR ? rp[HD] : NEG_INF;
-    const float M = wave_max(m);  // finite: row 0 of wave 0 holds the unit's first position
-    const float w = (m == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    const float Ls = wave_sum(lane < NR ? rp[HD + 1] * w : 0.f);
-    if (lane < NR) rp[HD + 2] = w;
-    if (lane == 0) {
-      hs[2 * h] = M;
-      hs[2 * h + 1] = Ls;
-    }
-  }
-  wg_barrier();
-
-  // The weighted sum over the rows of each pair of output dims of each head: NS lanes of a quad
-  // take every NS-th row (eight rows per batch of LDS reads) and add their sums by DPP. The
-  // quad's first lane then writes this unit's tagged partial (values, max, sum) or, for a single
-  // split, the attention output.
-  const int npair = G * HD / 2;
-  const int NS = npair * 4 <= kThreads ? 4 : (npair * 2 <= kThreads ? 2 : 1);  // uniform
-  const uint32_t tpart = tag_of(p, layer, kTagPart), to_tag = tag_of(p, layer, kTagO);
-  for (int t = tid; t < npair * NS; t += kThreads) {  // NS divides npair * NS: quads stay whole
-    const int pi = t / NS, sub = t - pi * NS;
-    const int h = pi / (HD / 2), d = 2 * (pi - h * (HD / 2));
-    const float* rp = wp + h * RS;
-    float A0 = 0.f, A1 = 0.f;
-    for (int r0 = sub; r0 < NR; r0 += 8 * NS) {  // NR / NS is a multiple of 8
-      float w[8];
-      float2 v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float* q = rp + (r0 + k * NS) * GMAX * RS;
-        w[k] = q[HD + 2];
-        v[k] = *reinterpret_cast<const float2*>(q + d);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        A0 = __builtin_fmaf(v[k].x, w[k], A0);
-        A1 = __builtin_fmaf(v[k].y, w[k], A1);
-      }
-    }
-    if (NS >= 2) {
-      A0 += dpp<0xB1>(A0);
-      A1 += dpp<0xB1>(A1);
-    }
-    if (NS >= 4) {
-      A0 += dpp<0x4E>(A0);
-      A1 += dpp<0x4E>(A1);
-    }
-    // every lane of the quad holds both sums now
-    const float M = hs[2 * h], Ls = hs[2 * h + 1];
-    if (S == 1) {
-      if (sub != 0) continue;
-      const float inv = 1.0f / Ls;
-      st_tag(p.to + ((g * G + h) * HD + d) / 2,
-             static_cast<uint32_t>(f32_to_bf16(A0 * inv)) | (static_cast<uint32_t>(f32_to_bf16(A1 * inv)) << 16),
-             to_tag);
-    } else {
-      // lanes 0 and 1 of the quad store the pair's two words with one store instruction, so a
-      // wave writes whole runs of consecutive words (whole cache sectors)
-      uint64_t* dst = p.tpart + (static_cast<size_t>(g * G + h) * p.s_cap + j) * (HD + 2);
-      if (NS >= 2) {
-        if (sub < 2) st_tag(dst + d + sub, __float_as_uint(sub == 0 ? A0 : A1), tpart);
-      } else {
-        st_tag(dst + d, __float_as_uint(A0), tpart);
-        st_tag(dst + d + 1, __float_as_uint(A1), tpart);
-      }
-      if (d == 0 && sub == 0) {
-        st_tag(dst + HD, __float_as_uint(M), tpart);
-        st_tag(dst + HD + 1, __float_as_uint(Ls), tpart);
-      }
-    }
-  }
-}
-
-
-// The form the kernel runs for a head_dim (see the measurements at the top of this section).
-template <int HD> constexpr bool kAttnTiles = HD == 64;
-template <int HD, int GMAX>
-using AttnRegs = std::conditional_t<kAttnTiles<HD>, AttnTileRegs<HD>, AttnRowRegs<GMAX>>;
-template <int HD, int GMAX>
-using AttnLds = std::conditional_t<kAttnTiles<HD>, AttnTileLds<HD, GMAX>, AttnRowLds<HD, GMAX>>;
-template <int HD, int GMAX>
-__device__ __forceinline__ void attention_prefetch(const KParams& p, int layer, AttnRegs<HD, GMAX>& R) {
-  if constexpr (kAttnTiles<HD>) attention_prefetch_tiles<HD>(p, layer, R);
-  else attention_prefetch_rows<HD, GMAX>(p, layer, R);
-}
-template <int HD, int GMAX>
-__device__ __forceinline__ void attention_stage(const KParams& p, int layer, float* smem, AttnRegs<HD, GMAX>& R) {
-  if constexpr (kAttnTiles<HD>) attention_stage_tiles<HD, GMAX>(p, layer, smem, R);
-  else attention_stage_rows<HD, GMAX>(p, layer, smem, R);
 }
 
 // The blocks of kv head g each merge one slice of the head's G * HD outputs over its S splits
@@ -1745,7 +1425,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;
   GemvRegs R;
-  AttnRegs<HD, GMAX> AR;
+  AttnRegs<HD> AR;
   bool ok = true;
   // end of a hand-off: the next stage's input is in LDS, or every thread leaves
   auto handoff_done = [&]() -> bool {
