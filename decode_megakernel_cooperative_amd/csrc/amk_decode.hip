@@ -32,18 +32,23 @@
 //    W4A16: sign-magnitude codes, eight per dword, laid out so that two masks turn a dword into
 //    eight fp8 (e4m3) subnormals of value q * 2^-9; gfx950's fp8-to-bf16 pair conversion and
 //    bf16 pair dot products then take two weights per instruction (1.375 VALU per weight).
+//    W4A16-G128: the same codes; a lane's 32 columns of a chunk lie in one 128-column group, so
+//    the lane's partial sum is multiplied by that group's fp16 scale before it joins the row.
 //  * Row pairs: rows are packed at load time so that rows i and i + hd/2 of one head (a RoPE
 //    pair) and rows n of gate and up (a SwiGLU pair) are adjacent; one wave computes both rows
 //    of a pair, so the RoPE / SwiGLU / residual epilogues need no cross-wave exchange.
 //  * Attention: split-KV over (kv head, position range) units, one unit per block. The G query
-//    heads of a kv head share every K/V load. Each 16-lane row (hd 128) or 8-lane row (hd 64)
-//    scores one position per step with DPP row reductions and keeps an online softmax in base-2
-//    units; all rows of the block then merge in LDS (one exp2 weight per row and head) into one
-//    tagged partial (values, max, sum) per unit; then every block of the kv head merges one
+//    heads of a kv head share every K/V load. Each wave takes 16-position tiles: K and V rows
+//    are loaded whole into a per-wave LDS tile, the G heads' scores and the weighted values are
+//    bf16 matrix-core products (q and the softmax weights split into high and low bf16 parts),
+//    and each head keeps an online softmax in base-2 units. The block's waves then merge in LDS
+//    into one tagged partial (values, max, sum) per unit; every block of the kv head merges one
 //    slice of the head's outputs over all splits by log-sum-exp weights (DPP segmented
 //    reductions) and writes it as tagged bf16 pairs. A context short enough for one split per
 //    kv head skips that second merge: the unit writes the normalised output itself.
-//  * No MFMA: batch-1 decode is a matrix-vector product, far below the MFMA ridge point.
+//  * Matrix cores for attention only: a batch-1 GEMV is a matrix-vector product, far below the
+//    MFMA ridge point, so the projections run on the VALU; attention's per-tile products (up to
+//    16 heads by 16 positions by hd) are small dense contractions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
