@@ -131,6 +131,24 @@ def blas_info() -> dict:
     return {"vendor": "unknown", "threads": os.cpu_count() or 1, "version": None}
 
 
+def end_to_end_greedy(torch, dec, first_token: int, pos0: int, n: int, stream) -> dict:
+    """Greedy decode driven from the host: each launch computes the argmax in the kernel
+    (amk_decode_step_greedy), and the host reads that token (a 4-byte device-to-host copy, which
+    waits for the launch) before it issues the next launch. So the per-token time includes the
+    launch, the argmax and one host round trip; the timed bench line queues its launches instead."""
+    tok_dev = torch.full((n + 1,), first_token, dtype=torch.int32, device=stream.device)
+    torch.cuda.synchronize()
+    got = []
+    t0 = time.perf_counter()
+    for i in range(n):
+        dec.step_greedy(tok_dev[i:i + 1], pos0 + i, next_token_out=tok_dev[i + 1:i + 2], stream=stream)
+        got.append(int(tok_dev[i + 1].item()))
+    us = (time.perf_counter() - t0) * 1e6 / n
+    dec.sync()
+    return {"us_per_token": round(us, 1), "steps": n, "positions": f"{pos0}-{pos0 + n - 1}",
+            "mode": "host-driven: in-kernel argmax, the host reads each token before the next launch"}
+
+
 def stage_trace(torch, D, dec, info, shape, tokens, pos0, n, stream) -> None:
     """Per-stage times of n steps from the kernel's own per-block stamps (amk_set_trace), as a
     table on stderr: per stage, the mean over blocks and the slowest block, averaged over the
@@ -247,6 +265,9 @@ def main() -> int:
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
     read_peak = measured_read_gbps(torch, dev)
     log(f"[bench] vendor bf16 GEMV (torch.mv) streams {read_peak:.0f} GB/s on this GPU")
+    e2e = end_to_end_greedy(torch, dec, tokens[0], pos0, min(32, steps), stream)
+    log(f"[bench] end-to-end greedy (host reads every token before the next launch): "
+        f"{e2e['us_per_token']:.1f} us/token over {e2e['steps']} steps")
     if args.stage_trace > 0:
         stage_trace(torch, D, dec, info, shape, tokens, pos0, min(args.stage_trace, steps), stream)
 
@@ -325,6 +346,7 @@ def main() -> int:
         "pct_of_measured_read": round(100 * achieved / read_peak, 2),
         "parity": parity,
         "cpu_baseline": cpu,
+        "e2e_greedy": e2e,
     }
     print(json.dumps(out), flush=True)
     dec.close()
