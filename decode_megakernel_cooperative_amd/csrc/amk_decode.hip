@@ -947,11 +947,15 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
 // ------------------------------------------------------------------------------------------
 
 // A unit (kv head g, split j) covers positions [t0, t1) in tiles of kAttnTile = 16 positions;
-// wave w takes tiles w, w + 8, w + 16, ... For a tile, a wave forms the scores of the G heads
-// with bf16 matrix-core products (S^T = Q K^T: q, in base-2 units, split into a bf16 high and low
-// part, so it keeps 16 significant bits; K is bf16), updates each head's online softmax, and adds
-// P V the same way (P split into high and low parts, V bf16). Every product is exact in fp32 and
-// the sums are fp32. The waves' (max, sum, values) then merge through LDS into the unit's partial.
+// wave w takes tiles w, w + 8, w + 16, ... For a tile, a wave forms the transposed scores of the
+// G heads with bf16 matrix-core products (S^T = K Q^T: q, in base-2 units, split into a bf16 high
+// and low part, so it keeps 16 significant bits; K is bf16), updates each head's online softmax,
+// and adds the transposed weighted values O^T += V^T P^T the same way (P split into high and low
+// parts, V bf16). Every product is exact in fp32 and the sums are fp32. In the transposed form a
+// lane holds one head (its column) at four positions: the head's tile maximum is a reduction over
+// the lane's 4 elements and the 4 lanes of that column, the weights P^T are already the B operand
+// of the value product, and the rescaling of the head's values stays inside the lane. The waves'
+// (max, sum, values) then merge through LDS into the unit's partial.
 //
 // K and V are loaded in whole position rows (hd / 8 lanes of 16 bytes per row, so one load
 // instruction reads 64 / (hd / 8) complete rows) and reach the MFMA operand layouts through a
@@ -979,17 +983,16 @@ struct AttnRegs {
 // has seen no position keeps weight 0 in the merge.
 constexpr float kScoreFloor = -1.0e30f;
 
-// LDS of the stage (byte offsets): per wave a K and a V tile [16][2 HD + 32 bytes], a P tile
-// [GMAX][16] fp32 and a result row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float
-// offset kQ) q of the G heads [G][HD] fp32 and K/V(pos) [2][HD] bf16. Matches attn_lds_bytes.
+// LDS of the stage (byte offsets): per wave a K and a V tile [16][2 HD + 32 bytes] and a result
+// row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float offset kQ) q of the G heads
+// [G][HD] fp32 and K/V(pos) [2][HD] bf16. Matches attn_lds_bytes.
 template <int HD, int GMAX>
 struct AttnLds {
   static constexpr int kVStride = 2 * HD + 32;  // padded: the 16 rows of a transposed read spread over the banks
   static constexpr int kRStride = HD + 4;
   static constexpr int kK = 0;
   static constexpr int kV = kK + kWaves * kAttnTile * kVStride;
-  static constexpr int kP = kV + kWaves * kAttnTile * kVStride;
-  static constexpr int kRes = kP + kWaves * GMAX * kAttnTile * 4;
+  static constexpr int kRes = kV + kWaves * kAttnTile * kVStride;
   static constexpr int kQ = (kRes + kWaves * GMAX * kRStride * 4) / 4;
 };
 
@@ -1061,7 +1064,6 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   uint8_t* vt = lds + Lds::kV + wave * kAttnTile * Lds::kVStride;
   uint8_t* kt = lds + Lds::kK + wave * kAttnTile * Lds::kVStride;
   constexpr int LPP = HD / 8, PPI = 64 / LPP;
-  float* pt = reinterpret_cast<float*>(lds + Lds::kP) + wave * GMAX * kAttnTile;
   float* res = reinterpret_cast<float*>(lds + Lds::kRes);
   const float* qs = smem + Lds::kQ;
   const uint16_t* kvp = reinterpret_cast<const uint16_t*>(qs + G * HD);  // K(pos) [HD], V(pos) [HD]
@@ -1085,15 +1087,11 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         ql[c][e] = static_cast<__bf16>(q - static_cast<float>(hi));
       }
     }
-    // per head 4 kb + r (element r of the result rows this lane holds): running max (uniform over
-    // the 16 lanes of the row), this lane's share of the running sum, and the values
-    float mrun[4], lrun[4];
+    // for head col (the lane's column): the running max (uniform over the head's 4 lanes), this
+    // lane's share of the running sum (its positions 4 kb .. 4 kb + 3 of every tile), and the
+    // values: element r of o[n] is dim n * 16 + 4 kb + r of head col
+    float mrun = kScoreFloor, lrun = 0.f;
     f32x4 o[NV];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mrun[r] = kScoreFloor;
-      lrun[r] = 0.f;
-    }
 #pragma unroll
     for (int n = 0; n < NV; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int t0 = a.t0, t1 = a.t1, ntiles = a.ntiles;
@@ -1113,52 +1111,52 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
         *reinterpret_cast<i32x4*>(vt + cpos * Lds::kVStride + lane * 16) =
             *reinterpret_cast<const i32x4*>(kvp + HD + lane * 8);
       }
-      // scores: element r of lane l is head 4 (l / 16) + r at position l % 16 of the tile
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+      // transposed scores: element r of lane l is position 4 kb + r of the tile for head col; the
+      // high and low parts of q accumulate apart (two independent chains), then add
+      f32x4 sh = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const bf16x8_t kc = *reinterpret_cast<const bf16x8_t*>(kt + col * Lds::kVStride + (c * 32 + kb * 8) * 2);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[c], kc, s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[c], kc, s, 0, 0, 0);
+        sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, qh[c], sh, 0, 0, 0);
+        sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, ql[c], sl, 0, 0, 0);
       }
-      const bool valid = t0 + tile * kAttnTile + col < t1;
+      const int pb = t0 + tile * kAttnTile + 4 * kb;  // the position of element 0
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = pb + r < t1 ? sh[r] + sl[r] : NEG_INF;
+      float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      tmax = fmaxf(tmax, xor_lane<16>(tmax));  // the head's other k blocks
+      tmax = fmaxf(tmax, xor_lane<32>(tmax));
+      const float mnew = fmaxf(mrun, tmax);
+      const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
       float pr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = valid ? s[r] : NEG_INF;
-        const float mnew = fmaxf(mrun[r], seg_max(sv, 16));
-        const float corr = __builtin_amdgcn_exp2f(mrun[r] - mnew);
-        pr[r] = __builtin_amdgcn_exp2f(sv - mnew);
-        lrun[r] = __builtin_fmaf(lrun[r], corr, pr[r]);
-        mrun[r] = mnew;
+      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - mnew);
+      lrun = __builtin_fmaf(lrun, corr, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+      mrun = mnew;
 #pragma unroll
-        for (int n = 0; n < NV; ++n) o[n][r] *= corr;
-      }
-      // P through this wave's LDS tile [head][position] into the A operand of P V (lane l: head
-      // l % 16, positions 4 (l / 16) ..), and the V tile through LDS [position][dim] into the B
-      // operand (lane l: dim l % 16 of chunk n, positions 4 (l / 16) ..). A wave's LDS accesses
-      // complete in order, so no barrier is needed.
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * kb + r < GMAX) pt[(4 * kb + r) * kAttnTile + col] = pr[r];
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(pt + min(col, GMAX - 1) * kAttnTile + kb * 4);
-      s16x4_t ah, al;
+      for (int n = 0; n < NV; ++n) o[n] *= corr;
+      // P^T as the B operand of V^T P^T (lane l: head col, positions 4 kb ..): the lane's own
+      // weights, split into high and low bf16 parts
+      s16x4_t ph, pl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = static_cast<__bf16>(pv[e]);
-        ah[e] = __builtin_bit_cast(short, hi);
-        al[e] = __builtin_bit_cast(short, static_cast<__bf16>(pv[e] - static_cast<float>(hi)));
+        const __bf16 hi = static_cast<__bf16>(pr[e]);
+        ph[e] = __builtin_bit_cast(short, hi);
+        pl[e] = __builtin_bit_cast(short, static_cast<__bf16>(pr[e] - static_cast<float>(hi)));
       }
-      // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of the
-      // 8 bytes addressed by lanes 4 e + i / 4 (e = 0..3). Lane 4 e + c of k block kb addresses
-      // position 4 kb + e, dims n * 16 + 4 c .., so lane i gets V[4 kb + e][n * 16 + i].
+      // V^T as the A operand (lane l: dim n * 16 + col, positions 4 kb ..) by ds_read_b64_tr_b16:
+      // within each group of 16 lanes, lane i receives element i % 4 of the 8 bytes addressed by
+      // lanes 4 e + i / 4 (e = 0..3). Lane 4 e + c of k block kb addresses position 4 kb + e, dims
+      // n * 16 + 4 c .., so lane i gets V[4 kb + e][n * 16 + i]. A wave's LDS accesses complete in
+      // order, so no barrier is needed between the tile writes and these reads.
       const int vrow = (kb * 4 + (col >> 2)) * Lds::kVStride + 8 * (col & 3);
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        const s16x4_t bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        const s16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4_t*)(vt + vrow + n * 32));
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, o[n], 0, 0, 0);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, o[n], 0, 0, 0);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, o[n], 0, 0, 0);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, o[n], 0, 0, 0);
       }
     };
 
@@ -1170,20 +1168,17 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
       attn_tile_load<HD>(a, kr, vr, tile + 3 * kWaves, R.b);
     }
 
-    // this wave's result per head: values, max, and the sum over the row's 16 lanes (waves with
+    // this wave's result per head: values, max, and the sum over the head's 4 lanes (waves with
     // no tile write max = floor and zeros, which the merge weighs 0)
+    float lsum = lrun + xor_lane<16>(lrun);
+    lsum += xor_lane<32>(lsum);
+    if (col < G) {
+      float* rw = res + (wave * GMAX + col) * Lds::kRStride;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * kb + r;
-      const float lsum = seg_sum(lrun[r], 16);
-      if (h < G) {
-        float* rw = res + (wave * GMAX + h) * Lds::kRStride;
-#pragma unroll
-        for (int n = 0; n < NV; ++n) rw[n * 16 + col] = o[n][r];
-        if (col == 0) {
-          rw[HD] = mrun[r];
-          rw[HD + 1] = lsum;
-        }
+      for (int n = 0; n < NV; ++n) *reinterpret_cast<f32x4*>(rw + n * 16 + 4 * kb) = o[n];
+      if (kb == 0) {
+        rw[HD] = mrun;
+        rw[HD + 1] = lsum;
       }
     }
   }
