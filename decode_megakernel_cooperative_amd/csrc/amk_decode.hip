@@ -984,8 +984,9 @@ struct AttnRegs {
 constexpr float kScoreFloor = -1.0e30f;
 
 // LDS of the stage (byte offsets): per wave a K and a V tile [16][2 HD + 32 bytes] and a result
-// row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float offset kQ) q of the G heads
-// [G][HD] fp32 and K/V(pos) [2][HD] bf16. Matches attn_lds_bytes.
+// row per head [GMAX][HD + 4] fp32 (values, max, sum); then (float offset kQ) q of the G heads as
+// bf16 high parts [G][HD] and low parts [G][HD], and K/V(pos) [2][HD] bf16. Matches
+// attn_lds_bytes.
 template <int HD, int GMAX>
 struct AttnLds {
   static constexpr int kVStride = 2 * HD + 32;  // padded: the 16 rows of a transposed read spread over the banks
@@ -1071,21 +1072,15 @@ __device__ __forceinline__ void attention_stage(const KParams& p, int layer, flo
   const int g = a.g, j = a.j;
 
   if (a.active) {
-    // q as the A operand (lane l: head l % 16, dims c * 32 + 8 (l / 16) ..), in base-2 units (so
-    // every softmax weight is one exp2), split into bf16 high and low parts; heads past G are 0
-    const float qscale = p.attn_scale * 1.4426950408889634f;
+    // q as the B operand of K Q^T (lane l: head l % 16, dims c * 32 + 8 (l / 16) ..), already in
+    // base-2 units and split into bf16 high and low parts by the q poll; heads past G are 0
+    const bf16x8_t* qhs = reinterpret_cast<const bf16x8_t*>(qs);
+    const bf16x8_t zero8 = __builtin_bit_cast(bf16x8_t, i32x4{0, 0, 0, 0});
     bf16x8_t qh[NC], ql[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const f32x4 q0 = col < G ? *reinterpret_cast<const f32x4*>(qs + col * HD + c * 32 + kb * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 q1 = col < G ? *reinterpret_cast<const f32x4*>(qs + col * HD + c * 32 + kb * 8 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float q = (e < 4 ? q0[e & 3] : q1[e & 3]) * qscale;
-        const __bf16 hi = static_cast<__bf16>(q);
-        qh[c][e] = hi;
-        ql[c][e] = static_cast<__bf16>(q - static_cast<float>(hi));
-      }
+      qh[c] = col < G ? qhs[(col * HD + c * 32 + kb * 8) / 8] : zero8;
+      ql[c] = col < G ? qhs[(G * HD + col * HD + c * 32 + kb * 8) / 8] : zero8;
     }
     // for head col (the lane's column): the running max (uniform over the head's 4 lanes), this
     // lane's share of the running sum (its positions 4 kb .. 4 kb + 3 of every tile), and the
@@ -1302,8 +1297,11 @@ __device__ __forceinline__ bool attention_merge_slice(const KParams& p, int laye
 // ------------------------------------------------------------------------------------------
 // the persistent decode kernel
 // ------------------------------------------------------------------------------------------
-// q of the unit's G heads (fp32) into qs[G][HD] and, for the unit that holds pos, K/V(pos)
-// (bf16 pairs of dims i, i + HD/2) into the bf16 area after it. Returns false if abandoned.
+// q of the unit's G heads into the q area as the score product's operands: q times the
+// attention scale and log2(e) (base-2 units, so every softmax weight is one exp2), split into a
+// bf16 high part [G][HD] and the bf16 of the remainder [G][HD] (each value converted once, by
+// the thread that polls it); for the unit that holds pos, K/V(pos) (bf16 pairs of dims i,
+// i + HD/2) into the bf16 area after it. Returns false if abandoned.
 template <int HD>
 __device__ __forceinline__ bool poll_q_kv(const KParams& p, int layer, float* qs) {
   const AttnUnit a = attn_unit<HD>(p);
@@ -1315,6 +1313,8 @@ __device__ __forceinline__ bool poll_q_kv(const KParams& p, int layer, float* qs
   const int oq = toff(p, p.tq) + a.g * G * HD * 8, ok_ = toff(p, p.tkv) + a.g * half * 8,
             ov = toff(p, p.tkv) + (p.nkv + a.g) * half * 8;
   uint16_t* kvp = reinterpret_cast<uint16_t*>(qs + G * HD);
+  uint32_t* qpair = reinterpret_cast<uint32_t*>(qs);  // bf16 pairs: high parts, then low parts
+  const float qscale = p.attn_scale * 1.4426950408889634f;
   return poll_block<2>(
       p, nq4 + 2 * nkv4, tag_of(p, layer, kTagQKV),
       [&](int qi) {
@@ -1322,8 +1322,14 @@ __device__ __forceinline__ bool poll_q_kv(const KParams& p, int layer, float* qs
       },
       [&](int, int qi, uint32_t x0, uint32_t x1) {
         if (qi < nq4) {
-          qs[2 * qi] = __uint_as_float(x0);
-          qs[2 * qi + 1] = __uint_as_float(x1);
+          const float a = __uint_as_float(x0) * qscale, b = __uint_as_float(x1) * qscale;
+          const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
+          const __bf16 al = static_cast<__bf16>(a - static_cast<float>(ah));
+          const __bf16 bl = static_cast<__bf16>(b - static_cast<float>(bh));
+          qpair[qi] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
+          qpair[G * HD / 2 + qi] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, al)) |
+                                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bl)) << 16);
         } else {
           const int r = qi - nq4;
           const int kvs = r < nkv4 ? 0 : 1;
@@ -1420,7 +1426,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   };
   stamp();
   float* xs = smem;                                  // GEMV input vector (swizzled)
-  float* qs = smem + AttnLds<HD, GMAX>::kQ;          // attention: q, K/V(pos)
+  float* qs = smem + AttnLds<HD, GMAX>::kQ;          // attention: q (bf16 high, low parts), K/V(pos)
   const int H = p.H, L = p.L;
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;

@@ -10,8 +10,8 @@ constexpr int kCtrStride = 32;         // 32 x 4 B = one 128 B line
 constexpr int kAttnTile = 16;          // positions per attention tile (one MFMA column block)
 
 // LDS bytes of the attention stage: per wave a K and a V tile of kAttnTile positions (rows padded
-// by 32 bytes) and one result row per head [gmax][hd + 4] fp32; then q of the G heads (fp32) and
-// K/V of the current position (bf16).
+// by 32 bytes) and one result row per head [gmax][hd + 4] fp32; then q of the G heads (bf16 high
+// and low parts, 4 bytes per value in all) and K/V of the current position (bf16).
 constexpr int attn_lds_bytes(int hd, int gmax, int G) {
   return 2 * kWaves * kAttnTile * (2 * hd + 32) + kWaves * gmax * (hd + 4) * 4 + G * hd * 4 + 4 * hd;
 }
