@@ -71,19 +71,10 @@ __device__ __forceinline__ float ldc(const float* p) {
 __device__ __forceinline__ unsigned ldc(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void ldc2(const float* p, float& a, float& b) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  a = __uint_as_float(static_cast<uint32_t>(v));
-  b = __uint_as_float(static_cast<uint32_t>(v >> 32));
-}
 __device__ __forceinline__ void stc(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stc(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stc16(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Tagged exchange word: payload in the low 32 bits, the tag of the stage that wrote it in the
@@ -123,13 +114,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ i32x4 ldbuf(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufCacheNT);
 }
-// Agent-coherent (sc1) 16-byte buffer load, for vectors written by other blocks in this launch.
+// Cache policy of the agent-coherent (sc1) 16-byte buffer loads that poll vectors written by
+// other blocks in this launch.
 constexpr int kBufCacheSC1 = 16;
-__device__ __forceinline__ f32x4 ldbuf_c(__amdgpu_buffer_rsrc_t rs, int voff) {
-  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kBufCacheSC1);
-  return f32x4{__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z), __int_as_float(v.w)};
-}
-
 
 // ------------------------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -204,16 +191,6 @@ __device__ __forceinline__ float seg_max(float v, int SP) {
   if (SP >= 16) v = fmaxf(v, dpp<0x140>(v));
   if (SP >= 32) v = fmaxf(v, xor_lane<16>(v));
   if (SP >= 64) v = fmaxf(v, xor_lane<32>(v));
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  v = fmaxf(v, xor_lane<16>(v));
-  v = fmaxf(v, xor_lane<32>(v));
   return v;
 }
 
