@@ -119,6 +119,28 @@ def test_large_query_groups(which, fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16])
+@pytest.mark.parametrize("which", ["mha-hd128", "mha-hd64"])
+def test_one_query_head_per_kv_head(which, fmt):
+    """Plain multi-head attention (as many kv heads as query heads): in the attention tiles only
+    one of the 16 head columns of the score and value products is a real head. Prompt steps from
+    an empty cache (one split per kv head), then steps on a prefilled cache with many splits."""
+    if which == "mha-hd128":
+        shape = W.ModelShape("mha-hd128", 512, 2, 4, 4, 128, 1024, 1000, False, 500000.0)
+    else:
+        shape = W.ModelShape("mha-hd64", 512, 2, 8, 8, 64, 1024, 1000, True, 10000.0)
+    dec, orc, kv = build(shape, fmt, 16, 0, seed0=13)
+    toks = W.gen_tokens(shape, 6, seed0=13)
+    res = run_teacher_forced(dec, orc, kv, shape, 0, toks, 4, check_kv=True)
+    _assert_gates(res, f"{which} fmt{fmt} fresh")
+    dec.close()
+    dec, orc, kv = build(shape, fmt, 420, 400, seed0=14)
+    tok = W.gen_tokens(shape, 1, seed0=14)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 400, [], 6, first_token=tok, check_kv=True)
+    _assert_gates(res, f"{which} fmt{fmt} prefilled")
+    dec.close()
+
+
 @pytest.mark.parametrize("which", ["hd128", "hd64"])
 def test_single_split_boundary(which):
     """A context of at most 128 positions at head_dim 128 (256 at head_dim 64: one or two
