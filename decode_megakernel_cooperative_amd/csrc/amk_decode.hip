@@ -779,32 +779,43 @@ __device__ __forceinline__ void epilogue(const KParams& p, int layer, int pr, fl
   }
 }
 
-// Issues the 8 loads of the item that starts at cursor c (advancing c by kCG slots), and for
-// format 3 the slots' group-scale dwords (lane L takes group L / 4 of the chunk). np = pairs
-// in the segment, base = first pair of the segment.
+// Issues the two loads of the chunk slot at cursor c (both rows of its pair) and for format 3 the
+// slot's group-scale dword (lane L takes group L / 4 of the chunk); advances c by one slot.
+// np = pairs in the segment, base = first pair of the segment.
+template <int FMT>
+__device__ __forceinline__ void issue_slot(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t gsr, const GemvPlan& g,
+                                           int base, int np, Cursor& c, i32x4& r0, i32x4& r1, uint32_t& gs) {
+  const int lane = __lane_id();
+  const bool v = c.ch < g.nch && c.k < np;
+  const int off = c.ch * 1024 + lane * 16;
+  const int voff = (v && off < g.RB) ? off : kOOB;
+  // uniform by construction; readfirstlane keeps the compiler from moving it to VGPRs
+  const int pr = v ? pidx(g, base + c.k) : 0;
+  const int soff = __builtin_amdgcn_readfirstlane(2 * pr * g.RB);
+  r0 = ldbuf(rs, voff, soff);
+  r1 = ldbuf(rs, voff, soff + g.RB);
+  if constexpr (FMT == 3) {
+    const int goff = __builtin_amdgcn_readfirstlane((pr * g.nch + c.ch) * 64);
+    gs = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(gsr, v ? (lane >> 2) * 4 : kOOB, goff, kBufCacheNT));
+  }
+  c.advance(g.cpp);
+}
+
+// Issues the kCG slots (8 loads, plus the format-3 scales) of the item that starts at cursor c.
 template <int FMT>
 __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t gsr, const GemvPlan& g,
                                            int base, int np, Cursor& c, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG],
                                            uint32_t (&gs)[kCG]) {
-  const int lane = __lane_id();
 #pragma unroll
-  for (int s = 0; s < kCG; ++s) {
-    const bool v = c.ch < g.nch && c.k < np;
-    const int off = c.ch * 1024 + lane * 16;
-    const int voff = (v && off < g.RB) ? off : kOOB;
-    // uniform by construction; readfirstlane keeps the compiler from moving it to VGPRs
-    const int pr = v ? pidx(g, base + c.k) : 0;
-    const int soff = __builtin_amdgcn_readfirstlane(2 * pr * g.RB);
-    r0[s] = ldbuf(rs, voff, soff);
-    r1[s] = ldbuf(rs, voff, soff + g.RB);
-    if constexpr (FMT == 3) {
-      const int goff = __builtin_amdgcn_readfirstlane((pr * g.nch + c.ch) * 64);
-      gs[s] = static_cast<uint32_t>(
-          __builtin_amdgcn_raw_buffer_load_b32(gsr, v ? (lane >> 2) * 4 : kOOB, goff, kBufCacheNT));
-    }
-    c.advance(g.cpp);
-  }
+  for (int s = 0; s < kCG; ++s) issue_slot<FMT>(rs, gsr, g, base, np, c, r0[s], r1[s], gs[s]);
 }
+
+// Quantized weights refill each chunk slot of an item right after its FMAs, so its loads leave
+// a slot earlier than a refill of the whole item after its last FMA (8B W8A16 0.8%, W4A16 1.3%,
+// 1B W8A16 1.4% faster per token); bf16 weights, with far fewer VALU operations per slot, refill
+// whole items (slot refills measured 0.5% slower there).
+template <int FMT>
+constexpr bool kSlotRefill = FMT != 0;
 
 // Accumulates the item at cursor c into (acc0, acc1); when a slot completes a pair, reduces it
 // over the wave and lane 0 runs the epilogue. Slots that read zeros add nothing.
@@ -812,11 +823,15 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, __amdgpu_b
 // activations of the slot at cursor c on entry and of the slot after this item's last one on
 // return. int8 slots read their own activations first: reading one slot ahead measured 2%
 // slower per token for int8 weights and 1% faster for bf16 and int4.
+//
+// With kSlotRefill, each slot's registers are refilled (cursor ci, two items ahead) as soon as
+// its FMAs are issued.
 template <int FMT, int EPI>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
-                                             const float* xlane, const i32x4 (&r0)[kCG], const i32x4 (&r1)[kCG],
-                                             const uint32_t (&gs)[kCG], float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
-                                             EpiState& st, XSlot<FMT>& xn, float* dp) {
+                                             const float* xlane, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG],
+                                             uint32_t (&gs)[kCG], float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
+                                             EpiState& st, XSlot<FMT>& xn, float* dp, __amdgpu_buffer_rsrc_t rs,
+                                             __amdgpu_buffer_rsrc_t gsr, Cursor& ci) {
   constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
@@ -833,6 +848,7 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
     __builtin_amdgcn_sched_barrier(0);
     chunk_fma<FMT>(r0[s], r1[s], xc, gs[s], acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kSlotRefill<FMT>) issue_slot<FMT>(rs, gsr, g, base, np, ci, r0[s], r1[s], gs[s]);
     if (c.ch == g.nch - 1 && c.k < np) {
       float y0 = wave_sum(acc0), y1 = wave_sum(acc1);
       acc0 = acc1 = 0.f;
@@ -909,11 +925,11 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
     load_x<FMT>(xlane, xn);  // slot 0 of the segment is chunk 0
     for (int it = 0; it < items; it += 2) {
       gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.sa, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
-                             dp);
-      gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
+                             dp, rs, gsr, ci);
+      if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
       gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
-                             dp);
-      gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
+                             dp, rs, gsr, ci);
+      if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
     }
   }
   return st;
