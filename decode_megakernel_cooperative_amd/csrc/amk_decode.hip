@@ -819,10 +819,10 @@ constexpr bool kSlotRefill = FMT != 0;
 
 // Accumulates the item at cursor c into (acc0, acc1); when a slot completes a pair, reduces it
 // over the wave and lane 0 runs the epilogue. Slots that read zeros add nothing.
-// bf16 and int4 slots issue their LDS reads one slot ahead of their FMAs: xn holds the
-// activations of the slot at cursor c on entry and of the slot after this item's last one on
-// return. int8 slots read their own activations first: reading one slot ahead measured 2%
-// slower per token for int8 weights and 1% faster for bf16 and int4.
+// Slots issue their LDS reads one slot ahead of their FMAs: xn holds the activations of the slot
+// at cursor c on entry and of the slot after this item's last one on return. (With slot refills,
+// reading ahead is also faster for int8 weights: 1B W8A16 2.1%, 8B 0.2% per token; with item
+// refills it had measured 2% slower there.)
 //
 // With kSlotRefill, each slot's registers are refilled (cursor ci, two items ahead) as soon as
 // its FMAs are issued.
@@ -835,15 +835,10 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
   constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
   for (int s = 0; s < kCG; ++s) {
-    XSlot<FMT> xc;
-    if constexpr (FMT == 1) {
-      load_x<FMT>(xlane + min(c.ch, g.nch - 1) * XCS, xc);
-    } else {
-      xc = xn;
-      Cursor cn = c;
-      cn.advance(g.cpp);
-      load_x<FMT>(xlane + min(cn.ch, g.nch - 1) * XCS, xn);
-    }
+    const XSlot<FMT> xc = xn;
+    Cursor cn = c;
+    cn.advance(g.cpp);
+    load_x<FMT>(xlane + min(cn.ch, g.nch - 1) * XCS, xn);
     // keep the scheduler from hoisting the conversions of all slots at once (register spills)
     __builtin_amdgcn_sched_barrier(0);
     chunk_fma<FMT>(r0[s], r1[s], xc, gs[s], acc0, acc1);
