@@ -141,6 +141,20 @@ def test_one_query_head_per_kv_head(which, fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128])
+def test_lm_head_in_two_segments(fmt):
+    """A vocabulary of 135168 gives every wave 33 lm_head row pairs: more than one 32-pair segment
+    (operand window) per wave, so the GEMV starts a second segment mid-stage (with its own window
+    and first two items)."""
+    shape = W.ModelShape("big-vocab", 512, 1, 4, 2, 128, 768, 135168, True, 500000.0)
+    assert shape.vocab // 2 > 32 * 2048
+    dec, orc, kv = build(shape, fmt, 24, 0, seed0=9)
+    toks = W.gen_tokens(shape, 4, seed0=9)
+    res = run_teacher_forced(dec, orc, kv, shape, 0, toks, 3, check_kv=True)
+    _assert_gates(res, f"big-vocab fmt{fmt}")
+    dec.close()
+
+
 @pytest.mark.parametrize("which", ["hd128", "hd64"])
 def test_single_split_boundary(which):
     """A context of at most 128 positions at head_dim 128 (256 at head_dim 64: one or two
