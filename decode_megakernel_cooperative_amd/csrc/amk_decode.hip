@@ -816,6 +816,12 @@ __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, __amdgpu_b
 // whole items (slot refills measured 0.5% slower there).
 template <int FMT>
 constexpr bool kSlotRefill = FMT != 0;
+// An odd item count leaves a zero item in the loop's last iteration. int4 stages skip it (a
+// branch on a uniform count): with one 2 KB chunk per row, QKV, O and gate/up have odd counts,
+// and skipping measured 1.7% faster per token for 8B W4A16. For int8 (only the down projection
+// has an odd count) the branch changes the compiler's load waits and measured 2% slower.
+template <int FMT>
+constexpr bool kSkipZeroItem = kInt4<FMT>;
 
 // Accumulates the item at cursor c into (acc0, acc1); when a slot completes a pair, reduces it
 // over the wave and lane 0 runs the epilogue. Slots that read zeros add nothing.
@@ -922,9 +928,11 @@ __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __
       gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.sa, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
                              dp, rs, gsr, ci);
       if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
-                             dp, rs, gsr, ci);
-      if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
+      if (!kSkipZeroItem<FMT> || it + 1 < items) {  // uniform
+        gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg, st,
+                               xn, dp, rs, gsr, ci);
+        if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
+      }
     }
   }
   return st;
