@@ -286,16 +286,19 @@ class OracleModel:
         return self.lm_head.apply(hf, self.accum)
 
     # --------------------------------------------------------------------------------------
-    def sensitivity(self, token: int, pos: int, kv: np.ndarray, reference: Optional[np.ndarray] = None) -> float:
+    def sensitivity(self, token: int, pos: int, kv: np.ndarray, reference: Optional[np.ndarray] = None,
+                    return_alt: bool = False):
         """max |logits(float32 sums) - logits(float64 sums)| for this step: how far two valid
-        summation orders of the same definition land apart. Leaves `kv` unchanged."""
+        summation orders of the same definition land apart. Leaves `kv` unchanged. With
+        return_alt, returns (that distance, the float64-sum logits)."""
         ref = reference if reference is not None else self.decode_step(token, pos, kv.copy())
         self.accum = np.float64
         try:
             alt = self.decode_step(token, pos, kv.copy())
         finally:
             self.accum = F32
-        return float(np.max(np.abs(ref - alt)))
+        d = float(np.max(np.abs(ref - alt)))
+        return (d, alt) if return_alt else d
 
     def prefill_logits(self, tokens: Sequence[int]) -> np.ndarray:
         """Independent full-sequence causal forward over `tokens` at positions 0..P-1 with a

@@ -46,6 +46,12 @@ class ParityResult:
     greedy_checked: int = 0
     greedy_mismatch: int = 0
     tokens: List[int] = field(default_factory=list)
+    # conditioned runs: the stated rule (oracle top-2 margin > 5e-2) as well, and the distances to
+    # the oracle with float64 sums (GPU, and the float32 oracle itself), worst over the steps
+    literal_checked: int = 0
+    literal_mismatch: int = 0
+    gpu_vs_f64: float = 0.0
+    f32_vs_f64: float = 0.0
 
 
 def top2_margin(lg: np.ndarray) -> float:
@@ -89,7 +95,9 @@ def run_teacher_forced(dec, orc, kv_np, shape, first_pos: int, prompt: List[int]
     res = ParityResult()
     res.tols = []
     res.stage_worst = []
-    res.steps = []  # conditioned runs: (pos, max|dlogit|, spread, oracle top-2 margin, same argmax, in window)
+    # conditioned runs: (pos, max|dlogit|, spread, oracle top-2 margin, same argmax, in window,
+    # max |GPU - oracle with float64 sums|)
+    res.steps = []
     tok = prompt[0] if prompt else first_token
     n = len(prompt) + n_greedy
     dump = None
@@ -117,10 +125,12 @@ def run_teacher_forced(dec, orc, kv_np, shape, first_pos: int, prompt: List[int]
         assert np.all(np.isfinite(g)), f"non-finite logits at pos {pos}"
         in_window = i >= len(prompt) and (greedy_window is None or i - len(prompt) < greedy_window)
         if conditioned:
-            sens = orc.sensitivity(tok, pos, kv_before, reference=o)
-            res.steps.append((pos, d, sens, top2_margin(o), bool(np.argmax(g) == np.argmax(o)), in_window))
+            sens, o64 = orc.sensitivity(tok, pos, kv_before, reference=o, return_alt=True)
+            d64 = float(np.max(np.abs(g - o64)))
+            res.steps.append((pos, d, sens, top2_margin(o), bool(np.argmax(g) == np.argmax(o)), in_window, d64))
             log(f"    pos {pos}: max|dlogit| {d:.2e}, oracle float32-vs-float64 spread {sens:.2e}, "
-                f"oracle top-2 margin {res.steps[-1][3]:.2e}, argmax {'same' if res.steps[-1][4] else 'DIFFERENT'}")
+                f"GPU vs float64 sums {d64:.2e}, oracle top-2 margin {res.steps[-1][3]:.2e}, "
+                f"argmax {'same' if res.steps[-1][4] else 'DIFFERENT'}")
         else:
             tol, margin = LOGIT_TOL, MARGIN
             res.tols.append(tol)
@@ -151,9 +161,14 @@ def run_teacher_forced(dec, orc, kv_np, shape, first_pos: int, prompt: List[int]
         tol, margin = conditioned_tolerance(spread)
         res.tols = [tol] * len(res.steps)
         lit = [st for st in res.steps if st[5] and st[3] > MARGIN]
+        res.literal_checked = len(lit)
+        res.literal_mismatch = sum(not st[4] for st in lit)
+        res.gpu_vs_f64 = max(st[6] for st in res.steps)
+        res.f32_vs_f64 = spread
         log(f"    workload spread {spread:.2e} -> tol {tol:.2e}, greedy margin {margin:.2e}; at the stated "
-            f"5e-2 margin: {len(lit)} steps, {sum(not st[4] for st in lit)} with another argmax")
-        for pos, d, sens, mg, same, win in res.steps:
+            f"5e-2 margin: {len(lit)} steps, {res.literal_mismatch} with another argmax; worst distance to the "
+            f"oracle with float64 sums: GPU {res.gpu_vs_f64:.2e}, float32 oracle {spread:.2e}")
+        for pos, d, sens, mg, same, win, _ in res.steps:
             assert d <= tol, f"pos {pos}: logits differ by {d:.3e} > {tol:.3e}"
             if win and mg > margin:
                 res.greedy_checked += 1

@@ -19,7 +19,18 @@ Two kinds of gate run on every workload:
    from one step to the next. So the gate is conditioned on the workload's spread, the largest
    such distance over the run, measured by the oracle alone: tol = max(2e-2, 2 x spread) and
    margin = max(5e-2, 2 x tol) (gpu_harness.conditioned_tolerance). Where the spread is below
-   1e-2 this is the stated 2e-2 / 5e-2 rule; the literal 5e-2 statistics are logged.
+   1e-2 this is the stated 2e-2 / 5e-2 rule.
+3. The stated greedy rule itself, asserted as well: at every teacher-forced step where the
+   oracle's top-2 margin exceeds 5e-2 (27 of 32 steps on the 1B and 8B W8A16 runs), the GPU's
+   argmax is the oracle's. The kernel is deterministic, so this is a fixed property of these
+   seeded inputs; a flip at a margin below 2 x tol would be a near-tie that both results, each
+   within tol of the oracle, may legitimately resolve either way, and the float64-sum distance
+   logged beside it (GPU and float32 oracle, each against the oracle with float64 sums) is what
+   tells such a flip from a defect.
+4. Distance to the oracle run with float64 sums: the GPU's worst max-abs distance to it is at
+   most 1.5 x the float32 oracle's own (measured 0.94-1.24 x on these workloads). Both are
+   float32 evaluations of the same definition in different summation orders, so the exact-sum
+   result is a common reference and neither should sit much farther from it than the other.
 """
 import gc
 
@@ -52,9 +63,14 @@ def test_full_size(key, steps):
     log(f"  {key}: {steps} steps, worst max|dlogit| {max(res.max_abs):.2e} (largest tol {max(res.tols):.2e}), "
         f"greedy {res.greedy_checked} checked / {res.greedy_mismatch} mismatched, "
         f"stage GEMV error / bound {max(res.stage_worst):.3f}")
+    log(f"  {key}: stated 5e-2 rule {res.literal_checked} checked / {res.literal_mismatch} mismatched; "
+        f"distance to the float64-sum oracle: GPU {res.gpu_vs_f64:.2e}, float32 oracle {res.f32_vs_f64:.2e}")
     assert res.greedy_mismatch == 0
+    assert res.literal_mismatch == 0
+    assert res.gpu_vs_f64 <= max(2e-2, 1.5 * res.f32_vs_f64), (res.gpu_vs_f64, res.f32_vs_f64)
     if steps >= 32:  # the expected top-2 gap of 128256 logits is ~0.1-0.3, so 32 steps always reach the rule
         assert res.greedy_checked >= 1
+        assert res.literal_checked >= 16
     dec.close()
     del dec, orc, kv
     gc.collect()
