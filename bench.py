@@ -300,13 +300,14 @@ def main() -> int:
             log(f"[bench] oracle step {i}: {t_steps[-1]:.2f}s, max|dlogit| {diffs[-1]:.2e}, "
                 f"oracle float32-vs-float64 spread {sens:.2e}, GPU vs float64 sums {d64s[-1]:.2e}")
         tol = max(2e-2, 2.0 * max(tols))
-        # second gate: the GPU sits no farther from the oracle run with float64 sums than 1.5x the
-        # float32 oracle does (both are float32 evaluations in different summation orders)
-        tol64 = max(2e-2, 1.5 * max(tols))
+        # second gate, against the oracle run with float64 sums: the GPU within 2x the float32
+        # oracle's distance to it (both are float32 evaluations in different summation orders;
+        # over two steps the spread itself varies ~2x, so the factor is that of the first gate)
+        tol64 = max(2e-2, 2.0 * max(tols))
         parity = {"max_abs_logit_diff": max(diffs), "tol": tol, "steps_checked": n_cpu,
                   "rule": "max(2e-2, 2 x largest oracle float32-vs-float64 spread over the checked steps)",
                   "max_abs_vs_float64_sums": max(d64s), "tol_vs_float64_sums": tol64,
-                  "rule_vs_float64_sums": "max(2e-2, 1.5 x that spread)",
+                  "rule_vs_float64_sums": "max(2e-2, 2 x that spread)",
                   "pass": bool(max(diffs) <= tol and max(d64s) <= tol64)}
         blas = blas_info()
         cpu = {"value": float(np.median(t_steps) * 1e6), "unit": "us/token", "cores": blas["threads"],
