@@ -57,7 +57,8 @@ class amk_info(ctypes.Structure):
     _fields_ = [("grid_blocks", ctypes.c_int32), ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("handoffs_per_step", ctypes.c_int32), ("weight_bytes", ctypes.c_int64),
                 ("scratch_bytes", ctypes.c_int64), ("max_splits", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("dump_layer_floats", ctypes.c_int64), ("dump_floats", ctypes.c_int64)]
+                ("dump_layer_floats", ctypes.c_int64), ("dump_floats", ctypes.c_int64),
+                ("gemv_item_slots", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -535,26 +535,30 @@ __device__ __forceinline__ bool vector_from_words(const KParams& p, const uint64
 // ------------------------------------------------------------------------------------------
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
-constexpr int kCG = 2;  // chunk slots per item: 2 rows x kCG x 16 B dwordx4 loads per lane
+// CG (a kernel template parameter, 1 or 2): chunk slots per item, so an item is 2 rows x CG x
+// 16 B dwordx4 loads per lane and a wave keeps two items (2 CG KB) in flight. Two slots stream the
+// Llama-3-8B shapes fastest; one slot, half the reads queued at each hand-off, is faster for
+// hidden sizes up to 2048 (the host picks by hidden size).
 constexpr int kSeg = 32; // pairs per operand window (lane j holds the operand of packed row 2*base + j)
 
 // Registers that carry a GEMV stage's operand window and first two items across the wait for
 // the stage's input vector.
+template <int CG>
 struct GemvRegs {
-  i32x4 a0[kCG], a1[kCG], b0[kCG], b1[kCG];
-  uint32_t sa[kCG], sb[kCG];  // group scales of the items' slots (format 3 only)
+  i32x4 a0[CG], a1[CG], b0[CG], b1[CG];
+  uint32_t sa[CG], sb[CG];  // group scales of the items' slots (format 3 only)
   float wA, wB;
 };
 
 // How one stage is split. A wave owns the contiguous pair range [pa, pb), processed in
 // segments of at most kSeg pairs. Inside a segment, pair k's chunks occupy slots
 // [k*cpp, k*cpp + nch) of a padded slot space (cpp = chunks per pair rounded so that items of
-// kCG slots never straddle a pair unevenly); an item is kCG consecutive slots. Slots past a
+// CG slots never straddle a pair unevenly); an item is CG consecutive slots. Slots past a
 // row's end or past the segment read zeros, so every item issues the same 8 loads.
 struct GemvPlan {
   int RB;   // bytes per row
   int nch;  // 1 KB chunks per row
-  int cpp;  // padded slots per pair: 1, 2 or 4 when nch <= kCG, else a multiple of kCG
+  int cpp;  // padded slots per pair: 1 or 2 when nch <= CG, else a multiple of CG
   int pa, pb;     // the wave's pairs, as local indices k in [pa, pb)
   int st0, sst;   // local index k is pair st0 + k * sst of the matrix
 };
@@ -564,12 +568,12 @@ __device__ __forceinline__ int pidx(const GemvPlan& g, int k) { return g.st0 + k
 // s = w * blocks + b and takes pairs s, s + NW, s + 2 NW, ... (NW = waves in the grid). At any
 // moment the grid streams one sliding window of the matrix, consecutive pairs going to
 // consecutive blocks (and so to different XCDs), and block b holds pair b of every stage.
-template <int FMT>
+template <int FMT, int CG>
 __device__ __forceinline__ GemvPlan gemv_plan(int K, int npairs, int wave) {
   GemvPlan g;
   g.RB = K * Fmt<FMT>::BITS / 8;
   g.nch = (g.RB + 1023) >> 10;
-  g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : g.nch <= kCG ? kCG : (g.nch + kCG - 1) / kCG * kCG;
+  g.cpp = g.nch <= 1 ? 1 : g.nch <= 2 ? 2 : (g.nch + CG - 1) / CG * CG;
   const int NW = gridDim.x * kWaves;
   const int sw = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
   g.pa = 0;
@@ -801,13 +805,13 @@ __device__ __forceinline__ void issue_slot(__amdgpu_buffer_rsrc_t rs, __amdgpu_b
   c.advance(g.cpp);
 }
 
-// Issues the kCG slots (8 loads, plus the format-3 scales) of the item that starts at cursor c.
-template <int FMT>
+// Issues the CG slots (4 CG loads, plus the format-3 scales) of the item that starts at cursor c.
+template <int FMT, int CG>
 __device__ __forceinline__ void gemv_issue(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t gsr, const GemvPlan& g,
-                                           int base, int np, Cursor& c, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG],
-                                           uint32_t (&gs)[kCG]) {
+                                           int base, int np, Cursor& c, i32x4 (&r0)[CG], i32x4 (&r1)[CG],
+                                           uint32_t (&gs)[CG]) {
 #pragma unroll
-  for (int s = 0; s < kCG; ++s) issue_slot<FMT>(rs, gsr, g, base, np, c, r0[s], r1[s], gs[s]);
+  for (int s = 0; s < CG; ++s) issue_slot<FMT>(rs, gsr, g, base, np, c, r0[s], r1[s], gs[s]);
 }
 
 // Quantized weights refill each chunk slot of an item right after its FMAs, so its loads leave
@@ -832,15 +836,15 @@ constexpr bool kSkipZeroItem = kInt4<FMT>;
 //
 // With kSlotRefill, each slot's registers are refilled (cursor ci, two items ahead) as soon as
 // its FMAs are issued.
-template <int FMT, int EPI>
+template <int FMT, int EPI, int CG>
 __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g, int base, int np, int layer,
-                                             const float* xlane, i32x4 (&r0)[kCG], i32x4 (&r1)[kCG],
-                                             uint32_t (&gs)[kCG], float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
+                                             const float* xlane, i32x4 (&r0)[CG], i32x4 (&r1)[CG],
+                                             uint32_t (&gs)[CG], float wA, float wB, Cursor& c, float& acc0, float& acc1, uint32_t tg,
                                              EpiState& st, XSlot<FMT>& xn, float* dp, __amdgpu_buffer_rsrc_t rs,
                                              __amdgpu_buffer_rsrc_t gsr, Cursor& ci) {
   constexpr int XCS = Fmt<FMT>::XCS;
 #pragma unroll
-  for (int s = 0; s < kCG; ++s) {
+  for (int s = 0; s < CG; ++s) {
     const XSlot<FMT> xc = xn;
     Cursor cn = c;
     cn.advance(g.cpp);
@@ -871,15 +875,15 @@ __device__ __forceinline__ void gemv_compute(const KParams& p, const GemvPlan& g
 }
 
 // Loads the operand window of the segment at `base` and issues the segment's first two items.
-template <int FMT, int EPI>
+template <int FMT, int EPI, int CG>
 __device__ __forceinline__ void gemv_segment_start(const KParams& p, __amdgpu_buffer_rsrc_t rs,
                                                    __amdgpu_buffer_rsrc_t gsr, const float* __restrict__ Sc,
                                                    const GemvPlan& g, int base, int np, bool rfe, bool two,
-                                                   GemvRegs& R) {
+                                                   GemvRegs<CG>& R) {
   load_window<FMT, EPI>(p, Sc, g, base, rfe, R.wA, R.wB);
   Cursor c{0, 0};
-  gemv_issue<FMT>(rs, gsr, g, base, np, c, R.a0, R.a1, R.sa);
-  if (two) gemv_issue<FMT>(rs, gsr, g, base, np, c, R.b0, R.b1, R.sb);
+  gemv_issue<FMT, CG>(rs, gsr, g, base, np, c, R.a0, R.a1, R.sa);
+  if (two) gemv_issue<FMT, CG>(rs, gsr, g, base, np, c, R.b0, R.b1, R.sb);
 }
 
 // Buffer resource over a format-3 matrix's group scales (npairs * nch * 64 bytes); for the
@@ -891,13 +895,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gscale_rsrc(const float* Sc, c
 
 // Issues the stage's operand window and first two items; called before the block polls the
 // stage's input vector, so HBM keeps streaming while the producers of that vector finish.
-template <int FMT, int EPI>
+template <int FMT, int EPI, int CG>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
-                                              GemvRegs& R) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+                                              GemvRegs<CG>& R) {
+  const GemvPlan g = gemv_plan<FMT, CG>(K, npairs, wave_id());
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
-  gemv_segment_start<FMT, EPI>(p, rs, gscale_rsrc<FMT>(Sc, g, npairs), Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe,
+  gemv_segment_start<FMT, EPI, CG>(p, rs, gscale_rsrc<FMT>(Sc, g, npairs), Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe,
                                true, R);
 }
 
@@ -905,33 +909,32 @@ __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* _
 // ahead of its use; the loop body is branch free apart from the per-pair epilogue, so loads
 // stay in flight across iterations. Returns the epilogue state of lane 0 (the wave's argmax for
 // the logits stage).
-template <int FMT, int EPI>
+template <int FMT, int EPI, int CG>
 __device__ __forceinline__ EpiState gemv_run(const KParams& p, const uint8_t* __restrict__ W,
                                          const float* __restrict__ Sc, int K, int npairs, const float* xs,
-                                         int layer, bool rfe, GemvRegs& R, uint32_t tg, float* dp) {
-  const GemvPlan g = gemv_plan<FMT>(K, npairs, wave_id());
+                                         int layer, bool rfe, GemvRegs<CG>& R, uint32_t tg, float* dp) {
+  const GemvPlan g = gemv_plan<FMT, CG>(K, npairs, wave_id());
   EpiState st{-__builtin_inff(), 0x7fffffff};
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
   const __amdgpu_buffer_rsrc_t gsr = gscale_rsrc<FMT>(Sc, g, npairs);
   const float* xlane = xs + __lane_id() * 4;
   for (int base = g.pa; base < g.pb; base += kSeg) {
     const int np = min(kSeg, g.pb - base);
-    if (base != g.pa) gemv_segment_start<FMT, EPI>(p, rs, gsr, Sc, g, base, np, rfe, true, R);
-    const int items = (np * g.cpp + kCG - 1) / kCG;
+    if (base != g.pa) gemv_segment_start<FMT, EPI, CG>(p, rs, gsr, Sc, g, base, np, rfe, true, R);
+    const int items = (np * g.cpp + CG - 1) / CG;
     Cursor ci{0, 0}, cc{0, 0};
-    for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
-    for (int s = 0; s < kCG; ++s) ci.advance(g.cpp);
+    for (int s = 0; s < 2 * CG; ++s) ci.advance(g.cpp);
     float acc0 = 0.f, acc1 = 0.f;
     XSlot<FMT> xn;
     load_x<FMT>(xlane, xn);  // slot 0 of the segment is chunk 0
     for (int it = 0; it < items; it += 2) {
-      gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.a0, R.a1, R.sa, R.wA, R.wB, cc, acc0, acc1, tg, st, xn,
-                             dp, rs, gsr, ci);
-      if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
+      gemv_compute<FMT, EPI, CG>(p, g, base, np, layer, xlane, R.a0, R.a1, R.sa, R.wA, R.wB, cc, acc0, acc1, tg, st,
+                                 xn, dp, rs, gsr, ci);
+      if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT, CG>(rs, gsr, g, base, np, ci, R.a0, R.a1, R.sa);
       if (!kSkipZeroItem<FMT> || it + 1 < items) {  // uniform
-        gemv_compute<FMT, EPI>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg, st,
-                               xn, dp, rs, gsr, ci);
-        if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
+        gemv_compute<FMT, EPI, CG>(p, g, base, np, layer, xlane, R.b0, R.b1, R.sb, R.wA, R.wB, cc, acc0, acc1, tg,
+                                   st, xn, dp, rs, gsr, ci);
+        if constexpr (!kSlotRefill<FMT>) gemv_issue<FMT, CG>(rs, gsr, g, base, np, ci, R.b0, R.b1, R.sb);
       }
     }
   }
@@ -1400,7 +1403,7 @@ __device__ __forceinline__ bool greedy_token(const KParams& p, const EpiState& s
   return ok;
 }
 
-template <int HD, int FMT, int GMAX>
+template <int HD, int FMT, int GMAX, int CG>
 __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float red[kWaves];
@@ -1426,7 +1429,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   const int H = p.H, L = p.L;
   const int qkv_pairs = (p.nq + 2 * p.nkv) * (HD / 2);
   const int qdim = p.nq * HD;
-  GemvRegs R;
+  GemvRegs<CG> R;
   AttnRegs<HD> AR;
   bool ok = true;
   // end of a hand-off: the next stage's input is in LDS, or every thread leaves
@@ -1440,7 +1443,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     return true;
   };
 
-  gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv, p.s_qkv, H, qkv_pairs, false, R);
+  gemv_prefetch<FMT, EPI_QKV, CG>(p, p.w_qkv, p.s_qkv, H, qkv_pairs, false, R);
   rmsnorm_embed_to_lds<FMT>(p, p.norm_in, xs, red, dump_at(p, 0, kDH));
   stamp();
   wg_barrier();
@@ -1452,7 +1455,7 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
       if (!handoff_done()) return;
     }
     // QKV GEMV -> RoPE; q, K/V(pos) as tagged words, K/V(pos) also into the cache
-    gemv_run<FMT, EPI_QKV>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
+    gemv_run<FMT, EPI_QKV, CG>(p, p.w_qkv + l * p.w_qkv_ls, p.s_qkv + l * p.s_qkv_ls, H, qkv_pairs, xs, l, false, R,
                            tag_of(p, l, kTagQKV), dump_at(p, l, kDQKV));
     attention_prefetch<HD, GMAX>(p, l, AR);
     wg_barrier();  // every wave is done with xs
@@ -1466,16 +1469,16 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     stamp();
     ok = attention_merge_slice<HD>(p, l);
     stamp();
-    gemv_prefetch<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, l == 0, R);
+    gemv_prefetch<FMT, EPI_RESID, CG>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, l == 0, R);
     wg_barrier();  // attention is done with LDS
     if (ok) ok = vector_from_words<FMT>(p, p.to, qdim, tag_of(p, l, kTagO), xs, dump_at(p, l, kDO));
     stamp();
     if (!handoff_done()) return;
 
     // O-projection + residual
-    gemv_run<FMT, EPI_RESID>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, xs, l, l == 0, R,
+    gemv_run<FMT, EPI_RESID, CG>(p, p.w_o + l * p.w_o_ls, p.s_o + l * p.s_o_ls, qdim, H / 2, xs, l, l == 0, R,
                              tag_of(p, l, kTagXO), dump_at(p, l, kDWO));
-    gemv_prefetch<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, false, R);
+    gemv_prefetch<FMT, EPI_SWIGLU, CG>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, false, R);
     wg_barrier();
     stamp();
     ok = norm_from_x<FMT>(p, p.norm_post + static_cast<size_t>(l) * H, tag_of(p, l, kTagXO), xs, red,
@@ -1484,9 +1487,9 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     if (!handoff_done()) return;
 
     // gate/up GEMV -> SwiGLU
-    gemv_run<FMT, EPI_SWIGLU>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, xs, l, false, R,
+    gemv_run<FMT, EPI_SWIGLU, CG>(p, p.w_gu + l * p.w_gu_ls, p.s_gu + l * p.s_gu_ls, H, p.F, xs, l, false, R,
                               tag_of(p, l, kTagM), dump_at(p, l, kDGU));
-    gemv_prefetch<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
+    gemv_prefetch<FMT, EPI_RESID, CG>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, false, R);
     wg_barrier();
     stamp();
     ok = vector_from_words16<FMT>(p, reinterpret_cast<const uint32_t*>(p.tm), p.F, tag_of(p, l, kTagM), xs);
@@ -1494,15 +1497,15 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
     if (!handoff_done()) return;
 
     // down GEMV + residual
-    gemv_run<FMT, EPI_RESID>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, xs, l, false, R,
+    gemv_run<FMT, EPI_RESID, CG>(p, p.w_d + l * p.w_d_ls, p.s_d + l * p.s_d_ls, p.F, H / 2, xs, l, false, R,
                              tag_of(p, l, kTagXD), dump_at(p, l, kDWD));
     if (l + 1 < L)
-      gemv_prefetch<FMT, EPI_QKV>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
+      gemv_prefetch<FMT, EPI_QKV, CG>(p, p.w_qkv + (l + 1) * p.w_qkv_ls, p.s_qkv + (l + 1) * p.s_qkv_ls, H, qkv_pairs,
                                   false, R);
     else if (FMT != 0 && p.lm_fmt == 0)  // quantized projections, bf16 lm_head
-      gemv_prefetch<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
+      gemv_prefetch<0, EPI_LOGITS, CG>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
     else
-      gemv_prefetch<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
+      gemv_prefetch<FMT, EPI_LOGITS, CG>(p, p.w_lm, p.s_lm, H, p.V / 2, false, R);
     wg_barrier();
     stamp();
   }
@@ -1512,29 +1515,45 @@ __global__ void __launch_bounds__(kThreads, 1) amk_decode_kernel(const KParams p
   else ok = norm_from_x<FMT>(p, p.norm_final, tag_of(p, L - 1, kTagXD), xs, red, dump_at(p, L, kDH));
   stamp();
   if (!handoff_done()) return;
-  const EpiState st = head16 ? gemv_run<0, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr)
-                             : gemv_run<FMT, EPI_LOGITS>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr);
+  const EpiState st = head16 ? gemv_run<0, EPI_LOGITS, CG>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr)
+                             : gemv_run<FMT, EPI_LOGITS, CG>(p, p.w_lm, p.s_lm, H, p.V / 2, xs, L, false, R, 0u, nullptr);
   wg_barrier();
   stamp();
   if (p.next_token != nullptr) greedy_token(p, st, smem, red, ired);
 }
 
-template __global__ void amk_decode_kernel<64, 0, 4>(const KParams);
-template __global__ void amk_decode_kernel<64, 1, 4>(const KParams);
-template __global__ void amk_decode_kernel<128, 0, 4>(const KParams);
-template __global__ void amk_decode_kernel<128, 1, 4>(const KParams);
-template __global__ void amk_decode_kernel<64, 0, 8>(const KParams);
-template __global__ void amk_decode_kernel<64, 1, 8>(const KParams);
-template __global__ void amk_decode_kernel<128, 0, 8>(const KParams);
-template __global__ void amk_decode_kernel<128, 1, 8>(const KParams);
-template __global__ void amk_decode_kernel<64, 2, 4>(const KParams);
-template __global__ void amk_decode_kernel<128, 2, 4>(const KParams);
-template __global__ void amk_decode_kernel<64, 2, 8>(const KParams);
-template __global__ void amk_decode_kernel<128, 2, 8>(const KParams);
-template __global__ void amk_decode_kernel<64, 3, 4>(const KParams);
-template __global__ void amk_decode_kernel<128, 3, 4>(const KParams);
-template __global__ void amk_decode_kernel<64, 3, 8>(const KParams);
-template __global__ void amk_decode_kernel<128, 3, 8>(const KParams);
+template __global__ void amk_decode_kernel<64, 0, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 0, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 4, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 8, 1>(const KParams);
+template __global__ void amk_decode_kernel<64, 0, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 0, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 1, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 0, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 1, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 2, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 2, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 4, 2>(const KParams);
+template __global__ void amk_decode_kernel<64, 3, 8, 2>(const KParams);
+template __global__ void amk_decode_kernel<128, 3, 8, 2>(const KParams);
 
 // Zeroes n 32-bit words (a model's scratch: error flag and exchange words) before the model is
 // used again after a failure; a kernel rather than a memset so that it is safe in graph capture.
@@ -1548,19 +1567,18 @@ __global__ void amk_clear_kernel(uint32_t* p, size_t n) {
 
 // host-visible handles of the kernel instantiations (defined in this translation unit)
 // fmt: 0 bf16, 1 int8, 2 int4 (row scales), 3 int4 (group scales) projection weights
-extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax) {
+extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax,
+                                                                                int cg) {
   using namespace amk;
-  const void* const t[2][2][4] = {
-      {{(const void*)&amk_decode_kernel<64, 0, 4>, (const void*)&amk_decode_kernel<64, 1, 4>,
-        (const void*)&amk_decode_kernel<64, 2, 4>, (const void*)&amk_decode_kernel<64, 3, 4>},
-       {(const void*)&amk_decode_kernel<64, 0, 8>, (const void*)&amk_decode_kernel<64, 1, 8>,
-        (const void*)&amk_decode_kernel<64, 2, 8>, (const void*)&amk_decode_kernel<64, 3, 8>}},
-      {{(const void*)&amk_decode_kernel<128, 0, 4>, (const void*)&amk_decode_kernel<128, 1, 4>,
-        (const void*)&amk_decode_kernel<128, 2, 4>, (const void*)&amk_decode_kernel<128, 3, 4>},
-       {(const void*)&amk_decode_kernel<128, 0, 8>, (const void*)&amk_decode_kernel<128, 1, 8>,
-        (const void*)&amk_decode_kernel<128, 2, 8>, (const void*)&amk_decode_kernel<128, 3, 8>}}};
-  if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 3) return nullptr;
-  return t[head_dim == 128][gmax == 8][fmt];
+#define AMK_K(HD, F, G, C) (const void*)&amk_decode_kernel<HD, F, G, C>
+#define AMK_K4(HD, G, C) {AMK_K(HD, 0, G, C), AMK_K(HD, 1, G, C), AMK_K(HD, 2, G, C), AMK_K(HD, 3, G, C)}
+  const void* const t[2][2][2][4] = {{{AMK_K4(64, 4, 1), AMK_K4(64, 8, 1)}, {AMK_K4(128, 4, 1), AMK_K4(128, 8, 1)}},
+                                     {{AMK_K4(64, 4, 2), AMK_K4(64, 8, 2)}, {AMK_K4(128, 4, 2), AMK_K4(128, 8, 2)}}};
+#undef AMK_K4
+#undef AMK_K
+  if ((head_dim != 64 && head_dim != 128) || (gmax != 4 && gmax != 8) || fmt < 0 || fmt > 3 || (cg != 1 && cg != 2))
+    return nullptr;
+  return t[cg - 1][head_dim == 128][gmax == 8][fmt];
 }
 
 extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle() {

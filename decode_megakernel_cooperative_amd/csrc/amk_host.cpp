@@ -16,7 +16,7 @@
 #include "amk.h"
 #include "amk_kparams.h"
 
-extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax);
+extern "C" __attribute__((visibility("hidden"))) const void* amk_kernel_handle(int head_dim, int fmt, int gmax, int cg);
 extern "C" __attribute__((visibility("hidden"))) const void* amk_clear_kernel_handle();
 extern "C" __attribute__((visibility("hidden"))) hipError_t amk_static_scratch(void** ptr, size_t* bytes);
 
@@ -144,6 +144,7 @@ struct amk_model {
   int grid = 0;
   int lds_bytes = 0;
   int gmax = 4;
+  int cg = 2;               // chunk slots per GEMV item of the kernel variant
   int s_cap = 1;
   uint32_t tag0 = 1;        // tag base of the next launch
   const void* kernel = nullptr;
@@ -394,7 +395,10 @@ int amk_load_weights(const amk_config* cfg, const uint16_t* const* t, int32_t n_
     // the GEMV input vector, or the attention stage's tiles, results, q and K/V(pos)
     const int64_t attn_b = amk::attn_lds_bytes(static_cast<int>(hd), m->gmax, G);
     m->lds_bytes = static_cast<int>(std::max(4 * xs_f, attn_b));
-    m->kernel = amk_kernel_handle(static_cast<int>(hd), kfmt, m->gmax);
+    // one-slot items (half the reads in flight at each hand-off) for hidden sizes up to 2048,
+    // two-slot items (the deeper stream) above
+    m->cg = c.hidden <= 2048 ? 1 : 2;
+    m->kernel = amk_kernel_handle(static_cast<int>(hd), kfmt, m->gmax, m->cg);
   }
   if (m->lds_bytes > 160 * 1024) { delete m; return fail(AMK_ERR_UNSUPPORTED, "LDS need exceeds 160 KB"); }
   if (!m->kernel) { delete m; return fail(AMK_ERR_UNSUPPORTED, "no kernel variant"); }
@@ -796,6 +800,7 @@ int amk_get_info(const amk_model* m, amk_info* info) {
   info->device = m->device;
   info->dump_layer_floats = m->dump_layer;
   info->dump_floats = m->dump_layer * m->cfg.n_layers + m->cfg.hidden;
+  info->gemv_item_slots = m->cg;
   return AMK_OK;
 }
 

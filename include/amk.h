@@ -94,6 +94,8 @@ typedef struct {
   int32_t device;               /* HIP device the model lives on                             */
   int64_t dump_layer_floats;    /* floats per layer of the per-stage dump (amk_set_dump)      */
   int64_t dump_floats;          /* floats of a whole dump: n_layers * dump_layer_floats + H  */
+  int32_t gemv_item_slots;      /* 1 KB chunk slots per row in a GEMV item of the kernel
+                                   variant: 1 for hidden <= 2048, else 2                     */
 } amk_info;
 
 /* Copies, packs, (for the quantized formats) quantizes and uploads a model to the current device.

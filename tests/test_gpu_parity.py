@@ -71,6 +71,26 @@ def test_hd128_gqa4_prefilled_multi_split(fmt):
     dec.close()
 
 
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128])
+def test_two_slot_items_wide_ragged(fmt):
+    """The kernel variant with two 1 KB chunk slots per GEMV item, which the library picks above
+    hidden 2048 (one slot at and below): a 2560-wide model with 4416-wide SwiGLU rows, so rows
+    span several chunks with a ragged last one and odd item counts, with a prefilled cache (several
+    KV splits). Checks the variant choice on both sides of the boundary, then the stage checks and
+    the logit and greedy gates."""
+    shape = W.ModelShape("wide-ragged", 2560, 2, 20, 5, 128, 4416, 1000, False, 500000.0)
+    dec, orc, kv = build(shape, fmt, 140, 100, seed0=11)
+    assert dec.info().gemv_item_slots == 2
+    narrow_shape = W.ModelShape("hd64-2048", 2048, 1, 32, 8, 64, 2048, 512, True, 500000.0)
+    narrow = D.Decoder(narrow_shape, W.gen_weights(narrow_shape, 11), fmt, 16)
+    assert narrow.info().gemv_item_slots == 1
+    narrow.close()
+    tok = W.gen_tokens(shape, 1, seed0=11)[0]
+    res = run_teacher_forced(dec, orc, kv, shape, 100, [], 12, first_token=tok, check_kv=True, stage_steps=(0, 11))
+    _assert_gates(res, f"wide-ragged fmt{fmt}")
+    dec.close()
+
+
 def test_g3_hd64_long_prefill_w8a16():
     """G = 3 (SmolLM2-like grouping), head_dim 64, prefill 1500: many splits per kv head."""
     shape = W.ModelShape("g3-hd64", 384, 2, 6, 2, 64, 1024, 2048, True, 10000.0)
