@@ -1,7 +1,8 @@
 """GPU test of amk_decode_step_noalloc (the step whose exchange words live in the library's
 static device array): through the C ABI, its logits and KV writes equal amk_decode_step's bit
-for bit, on two calls in a row, the second with a smaller model and a shorter context (so it
-reuses a smaller part of the array that the first call left written)."""
+for bit, on calls in a row, each with a smaller model and a shorter context than the one before
+(so it reuses a smaller part of the array that the earlier calls left written). The first model
+is wide enough for the kernel variant with two-slot GEMV items, the others use one-slot items."""
 import pytest
 import torch
 
@@ -34,10 +35,20 @@ def _compare(a, b, tok, pos):
 
 
 def test_noalloc_step_matches_the_allocating_step():
+    wide = W.ModelShape("wide-ragged", 2560, 2, 20, 5, 128, 4416, 1000, False, 500000.0)
     big = W.ModelShape("hd128-gqa4", 512, 3, 8, 2, 128, 1376, 1000, False, 500000.0)
     small = W.ModelShape("hd64-gqa3", 576, 2, 9, 3, 64, 1536, 800, True, 10000.0)
+    a, b = _pair(wide, D.AMK_W8A16, 210, 200, 10)
+    assert a.info().gemv_item_slots == 2
+    wide_bytes = a.info().scratch_bytes
+    for i, t in enumerate(W.gen_tokens(wide, 2, seed0=10)):  # several splits per kv head
+        _compare(a, b, t, 200 + i)
+    a.close()
+    b.close()
     a, b = _pair(big, D.AMK_W8A16, 340, 300, 11)
+    assert a.info().gemv_item_slots == 1
     big_bytes = a.info().scratch_bytes
+    assert big_bytes < wide_bytes
     toks = W.gen_tokens(big, 3, seed0=11)
     for i, t in enumerate(toks):  # several splits per kv head: partials and merge words in use
         _compare(a, b, t, 300 + i)
@@ -54,4 +65,4 @@ def test_noalloc_step_matches_the_allocating_step():
     assert e.value.status == D.amk.AMK_ERR_INVALID_ARG
     a.close()
     b.close()
-    log("  no-alloc step: bit-identical to amk_decode_step on both models")
+    log("  no-alloc step: bit-identical to amk_decode_step on all three models")
