@@ -71,7 +71,7 @@ def test_hd128_gqa4_prefilled_multi_split(fmt):
     dec.close()
 
 
-@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W4A16, D.AMK_W4A16_G128])
+@pytest.mark.parametrize("fmt", [D.AMK_BF16, D.AMK_W8A16, D.AMK_W8A16_BF16_HEAD, D.AMK_W4A16, D.AMK_W4A16_G128])
 def test_two_slot_items_wide_ragged(fmt):
     """The kernel variant with two 1 KB chunk slots per GEMV item, which the library picks above
     hidden 2048 (one slot at and below): a 2560-wide model with 4416-wide SwiGLU rows, so rows
