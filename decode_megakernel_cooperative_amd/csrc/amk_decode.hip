@@ -894,15 +894,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gscale_rsrc(const float* Sc, c
 }
 
 // Issues the stage's operand window and first two items; called before the block polls the
-// stage's input vector, so HBM keeps streaming while the producers of that vector finish.
+// stage's input vector, so HBM keeps streaming while the producers of that vector finish. With
+// two-slot items the second item leaves about 0.2 us (512 clocks) after the first: the hand-off
+// words that the slowest producers store at this moment wait at the memory side behind the reads
+// the grid has in flight, and half of this CU's reads are not yet among them (Llama-3-8B shapes
+// 0.2-0.7% faster per token; longer delays, and any delay with one-slot items, measured slower).
 template <int FMT, int EPI, int CG>
 __device__ __forceinline__ void gemv_prefetch(const KParams& p, const uint8_t* __restrict__ W,
                                               const float* __restrict__ Sc, int K, int npairs, bool rfe,
                                               GemvRegs<CG>& R) {
   const GemvPlan g = gemv_plan<FMT, CG>(K, npairs, wave_id());
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(W, static_cast<uint32_t>(2 * npairs) * g.RB);
-  gemv_segment_start<FMT, EPI, CG>(p, rs, gscale_rsrc<FMT>(Sc, g, npairs), Sc, g, g.pa, min(kSeg, g.pb - g.pa), rfe,
-                               true, R);
+  const __amdgpu_buffer_rsrc_t gsr = gscale_rsrc<FMT>(Sc, g, npairs);
+  const int np = min(kSeg, g.pb - g.pa);
+  gemv_segment_start<FMT, EPI, CG>(p, rs, gsr, Sc, g, g.pa, np, rfe, CG == 1, R);
+  if constexpr (CG == 2) {
+    __builtin_amdgcn_s_sleep(8);
+    Cursor c{0, 0};
+    for (int s = 0; s < CG; ++s) c.advance(g.cpp);
+    gemv_issue<FMT, CG>(rs, gsr, g, g.pa, np, c, R.b0, R.b1, R.sb);
+  }
 }
 
 // Runs the stage. Items alternate between the two register buffers, each refilled two items
