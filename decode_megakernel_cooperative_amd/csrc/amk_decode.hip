@@ -22,7 +22,11 @@
 //    flag and every block leaves the kernel.
 //  * Prefetch across a hand-off: before a block starts polling a stage's input vector it issues
 //    that stage's operand window (row scales, RoPE tables or residual) and its first two weight
-//    items into registers; attention issues its K/V loads before q arrives.
+//    items into registers; attention issues its K/V loads before q arrives. A hand-off's words
+//    reach the other blocks through the memory side, behind the weight reads in flight, so the
+//    depth in flight is a trade-off: an item is one 1 KB chunk slot per row for hidden sizes up to
+//    2048 and two above (a template parameter), and with two-slot items the second prefetched
+//    item leaves a little after the first.
 //  * Activations: the GEMV input vector of a stage (RMSNorm output, attention output, SwiGLU
 //    output) is staged in LDS as fp32 holding bf16-rounded values (as bf16 for int4 weights),
 //    in a swizzled layout so the 16-byte LDS reads of a lane per weight chunk are bank-conflict
