@@ -11,7 +11,8 @@ Two kinds of gate run on every workload:
    bf16 ulp, RoPE and the residual adds to the same fp32 operations, the K/V written at the
    position within one bf16 ulp.
 2. End to end, teacher forced, over 32 steps (Llama-3.2-1B and Llama-3-8B W8A16) or 8 steps
-   (8B bf16, 8B W8A16 at 32k, 8B W4A16 with row and with group scales): logits within tol of the oracle at every step, and
+   (8B bf16, 8B W8A16 at 32k, 8B W8A16 with a bf16 lm_head, 8B W4A16 with row and with group
+   scales): logits within tol of the oracle at every step, and
    identical greedy tokens wherever the oracle's top-2 margin exceeds `margin`. At these widths the
    max-abs over 128256 logits is sensitive to summation order: two valid orders of the oracle
    itself (float32 vs float64 sums) land 2-5e-2 apart on the 1B model and ~6-11e-2 apart on the
@@ -47,6 +48,7 @@ CASES = [
     ("llama3-8b-w8a16-ctx4096", 32),
     ("llama3-8b-bf16-ctx4096", 8),
     ("llama3-8b-w8a16-ctx32768", 8),
+    ("llama3-8b-w8a16hb-ctx4096", 8),
     ("llama3-8b-w4a16-ctx4096", 8),
     ("llama3-8b-w4a16g-ctx4096", 8),
 ]
