@@ -364,7 +364,7 @@ __device__ __forceinline__ bool poll_block(const KParams& p, int nquads, uint32_
       unsigned it = 0;
       while (pend != 0u) {
         if (!wait_ok(p, ++it, t_start)) return false;
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(0);
 #pragma unroll
         for (int b = 0; b < VB; ++b)
           if (pend & (1u << b))
@@ -418,7 +418,7 @@ __device__ __forceinline__ bool vector_from_words16(const KParams& p, const uint
       unsigned it = 0;
       while (pend != 0u) {
         if (!wait_ok(p, ++it, t_start)) return false;
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(0);
 #pragma unroll
         for (int b = 0; b < VB; ++b)
           if (pend & (1u << b))
